@@ -1,0 +1,193 @@
+/*
+ * idx.h — C ABI of the MI355X (gfx950) DSA lightning-indexer top-k library (libidx.so).
+ *
+ * The operation (LiteTopK prefill indexer page, sgl-project/sglang#47469, introduction
+ * and section 1; ROCm DSA indexer top-k page, sgl-project/sglang#37591):
+ *
+ *   For every query row r and every key s the row can see (ks[r] <= s < ke[r]):
+ *       score[r, s] = kscale[s] * sum_h w[r, h] * max(q[r, h] . k[s], 0)
+ *   (MQA: one key vector per position shared by all heads), then return the exact
+ *   top-k keys of the row: fp32 value descending, -0.0 == +0.0, ties to the lower key
+ *   index.  Indices are relative to ks[r]; rows that see fewer than k keys return all
+ *   of them followed by -1.  The order of the indices inside a row is unspecified.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked (host).  The library never frees,
+ *     keeps or allocates device memory: the caller owns every buffer, including the
+ *     workspace, whose size comes from the matching *_workspace query.
+ *   - Alignment (error IDX_EALIGN): q and k 16 bytes (they are read as 16-byte vectors),
+ *     workspaces 256 bytes, every other device pointer its element size.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  All work is
+ *     enqueued on it, asynchronously; the call returns before the GPU finishes unless
+ *     stated otherwise.  The device used is the current HIP device of the calling thread.
+ *   - Return value: IDX_OK (0) or a negative error code; idx_strerror() gives text.
+ *     Argument errors are detected on the host before anything is enqueued, so a
+ *     failed call leaves outputs untouched.  The boundary never throws or aborts.
+ *   - Sizes: rows up to 2^31-1, keys per row up to 2^31-1, pitches and offsets int64.
+ */
+#ifndef IDX_H_
+#define IDX_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ error codes */
+#define IDX_OK 0
+#define IDX_EINVAL (-1) /* null pointer, bad size, k out of range, heads/head_dim unsupported */
+#define IDX_EFMT (-2)   /* format and pointers disagree (e.g. MXFP4 without block scales) */
+#define IDX_EALIGN (-3) /* a device pointer is misaligned (see Alignment above) */
+#define IDX_EWS (-4)    /* workspace smaller than the *_workspace query returned */
+#define IDX_EHIP (-5)   /* a HIP runtime call or kernel launch failed */
+#define IDX_ENODEV (-6) /* no usable gfx950 device is current */
+
+/* ------------------------------------------------------------------ limits */
+#define IDX_HEAD_DIM 128  /* head_dim of q and k */
+#define IDX_MAX_TOPK 2048 /* largest k (the DSA indexers keep 512..2048 keys) */
+#define IDX_PAGE 64       /* tokens per page of a paged K cache */
+
+/* Operand format, shared by q and k. */
+typedef enum idx_fmt {
+  IDX_FMT_E4M3 = 1,  /* OCP FP8 E4M3FN, one byte per element */
+  IDX_FMT_MXFP4 = 2  /* OCP MXFP4: e2m1 codes, two per byte (element 2i in the low
+                        nibble), plus one e8m0 scale per 32 consecutive head_dim
+                        elements (4 per head or key) */
+} idx_fmt;
+
+/* Test hooks that force the rare paths of idx_fused_topk from the host (NULL in
+ * production).  None of them changes the result, only the route to it. */
+typedef struct idx_debug {
+  int32_t cap;            /* > 0: candidate-slab capacity per row instead of 4*k */
+  int32_t threshold_mode; /* 0 sampled; 1 = +inf (no candidates: every sampled row
+                             underflows and falls back); 2 = -inf (every visible key is a
+                             candidate: rows with more than cap keys overflow) */
+  int32_t threshold_row_mod; /* > 0: apply threshold_mode only to rows r with
+                                r % threshold_row_mod == 0 */
+  int32_t reserved;
+} idx_debug;
+
+/* One indexer problem.  Layouts are row-major and densely packed.
+ *   q        E4M3: u8 [rows][heads][128];  MXFP4: u8 [rows][heads][64]
+ *   q_sf     MXFP4 only: e8m0 u8 [rows][heads][4]; must be NULL for E4M3
+ *   k        contiguous: E4M3 u8 [num_keys][128] / MXFP4 u8 [num_keys][64]
+ *            paged (E4M3 only): u8 [num_keys/64][64][128] (num_keys = pages * 64)
+ *   k_sf     MXFP4 only: e8m0 u8 [num_keys][4]; must be NULL for E4M3
+ *   k_scale  optional fp32 [num_keys] (per key, or per physical slot when paged),
+ *            > 0; NULL means 1.0.  Multiplies the score (equivalently the key).
+ *   w        bf16 bits [rows][heads], >= 0
+ *   ks, ke   int32 [rows]: row r sees logical keys [ks[r], ke[r]), 0 <= ks <= ke.
+ *            Contiguous: ke <= num_keys.  Paged: ke <= max_pages * 64.
+ *   page_table  NULL = contiguous K.  Else int32 [num_req][max_pages]: logical key s of
+ *            request q lives in physical slot page_table[q][s / 64] * 64 + s % 64
+ *            (LiteTopK page, section 3).  Entries past a request's last visible page are
+ *            never read.
+ *   row_req  paged only: int32 [rows], request of each row, in [0, num_req).
+ *   Values the library cannot check on the host (ranges inside device arrays, NaN
+ *   codes, page ids) must be valid; invalid ones give undefined results.
+ */
+typedef struct idx_problem {
+  int32_t rows;
+  int32_t heads;    /* 32 or 64 */
+  int32_t head_dim; /* must be IDX_HEAD_DIM */
+  int32_t fmt;      /* idx_fmt */
+  const void* q;
+  const uint8_t* q_sf;
+  const void* k;
+  const uint8_t* k_sf;
+  const float* k_scale;
+  const uint16_t* w;
+  const int32_t* ks;
+  const int32_t* ke;
+  int64_t num_keys;
+  const int32_t* page_table;
+  const int32_t* row_req;
+  int32_t num_req;
+  int32_t max_pages;
+  const idx_debug* debug; /* (host) NULL in production */
+} idx_problem;
+
+/* Route taken by idx_fused_topk (host struct, filled when a pointer is passed). */
+typedef struct idx_stats {
+  int32_t rows;            /* rows of the problem */
+  int32_t rows_store_all;  /* rows that see <= cap keys: every key is a candidate */
+  int32_t rows_sampled;    /* rows filtered by a sampled threshold */
+  int32_t fallback_rows;   /* rows re-scored and selected over the whole row because the
+                              slab under- or overflowed */
+  int32_t max_count;       /* largest candidate count of a row (may exceed cap) */
+  int32_t min_count;       /* smallest candidate count among sampled rows */
+  int64_t total_count;     /* sum of candidate counts */
+  int32_t cap;             /* slab capacity per row */
+  int32_t sample_stride;   /* odd sample stride S */
+  int32_t sample_keys;     /* sample slots per row (one every S keys) */
+  int32_t reserved;
+} idx_stats;
+
+/* ------------------------------------------------------------------ scoring
+ * idx_score — materialised scores (the role of DeepGEMM mqa_logits, LiteTopK page,
+ * introduction).  Writes out[r * ld + (s - ks[r])] (fp32) for every visible key s of
+ * row r and nothing else.  ld >= max over rows of (ke - ks); out: fp32 [rows][ld].
+ * Scores are bitwise identical to those idx_fused_topk selects from (same scoring
+ * core; LiteTopK page, section 1: only the epilogue differs).                        */
+int idx_score(const idx_problem* p, float* out, int64_t ld, void* stream);
+
+/* ------------------------------------------------------------------ selection
+ * idx_select — exact top-k over materialised fp32 rows (ROCm DSA indexer top-k page:
+ * fp32 radix histogram, exact tie refinement, full-row rescan when the tie buffer
+ * overflows, rows split over several workgroups at low batch).
+ *   scores   fp32 [rows][ld]; row r's candidates are scores[r*ld + row_start[r] + j],
+ *            0 <= j < len[r]  (row_start may be NULL = 0; row_start + len <= ld)
+ *   len      int32 [rows], 0 <= len <= ld
+ *   k        1 .. IDX_MAX_TOPK
+ *   out_idx  int32 [rows][k]: the selected j (relative to row_start), -1 padded
+ *   ws       workspace of idx_select_workspace(rows, ld, k) bytes (may be NULL when
+ *            that is 0)
+ * NaN scores give undefined results.                                                 */
+int idx_select(const float* scores, int64_t ld, const int32_t* row_start, const int32_t* len,
+               int32_t rows, int32_t k, int32_t* out_idx, void* ws, size_t ws_bytes,
+               void* stream);
+
+/* Same as idx_select with the number of workgroups per row forced: split = 0 one
+ * workgroup per row, split >= 2 that many (at most 32).  The result is identical. */
+int idx_select_split(const float* scores, int64_t ld, const int32_t* row_start,
+                     const int32_t* len, int32_t rows, int32_t k, int32_t* out_idx, void* ws,
+                     size_t ws_bytes, int32_t split, void* stream);
+
+/* Workgroups per row idx_select uses for `rows` rows of pitch `row_len` on a device
+ * with `cu_count` compute units: g = min(cu_count / rows, 32), or 0 (one workgroup per
+ * row) when g < 4 or row_len < 65536 (ROCm top-k page, row_split).  Host only.     */
+int32_t idx_row_split(int32_t rows, int64_t row_len, int32_t cu_count);
+
+/* Bytes of workspace idx_select / idx_select_split need (the larger of both routes). */
+size_t idx_select_workspace(int32_t rows, int64_t ld, int32_t k);
+
+/* ------------------------------------------------------------------ fused top-k
+ * idx_fused_topk — the no-logits path (LiteTopK page, "sampled threshold", sections
+ * 1-2; exactness as in the ROCm top-k page).  Per row: a threshold T_r from an
+ * odd-stride single-key sample of the row's own scores; one pass scores every visible
+ * key and appends only (score, key) with score >= T_r to a per-row candidate slab with
+ * a count (rows that see <= cap keys keep every key); an exact radix select over the
+ * slab; rows whose slab under- or overflowed are re-scored and selected exactly.  The
+ * result equals idx_select over idx_score's output, bit for bit.
+ *   out_idx  int32 [rows][k], indices relative to ks[r], -1 padded
+ *   ws       workspace of idx_fused_workspace(p, k) bytes
+ *   stats    (host) optional; when non-NULL the call waits for the stream and fills it.
+ */
+int idx_fused_topk(const idx_problem* p, int32_t k, int32_t* out_idx, void* ws, size_t ws_bytes,
+                   idx_stats* stats, void* stream);
+
+/* Bytes of workspace idx_fused_topk needs for this problem shape and k (host only;
+ * reads only the scalar fields of p).  Returns 0 for invalid arguments.            */
+size_t idx_fused_workspace(const idx_problem* p, int32_t k);
+
+/* ------------------------------------------------------------------ misc */
+const char* idx_strerror(int code);
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t idx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* IDX_H_ */

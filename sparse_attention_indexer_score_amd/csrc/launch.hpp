@@ -1,0 +1,59 @@
+// Host-side launchers of the gfx950 kernels (defined next to the kernels they launch).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace idx {
+
+// Raw problem description (device pointers), validated by the C ABI layer.
+struct DevProblem {
+  int32_t rows, heads, fmt;
+  const uint8_t* q;
+  const uint8_t* q_sf;
+  const uint8_t* k;
+  const uint8_t* k_sf;
+  const float* k_scale;
+  const uint16_t* w;
+  const int32_t* ks;
+  const int32_t* ke;
+  int64_t num_keys;
+  const int32_t* page_table;
+  const int32_t* row_req;
+  int32_t num_req, max_pages;
+  int64_t key_span;  // logical key space: num_keys (contiguous) or max_pages * 64 (paged)
+};
+
+// Per-call plan of the fused path (sizes and workspace carve-up).
+struct FusedPlan {
+  int32_t k, cap, stride, ns, fb_blocks;
+  int32_t debug_mode, debug_row_mod;
+  int64_t scratch_ld;
+  // workspace regions
+  float* thr;
+  int32_t* cnt;
+  long long* stats;  // kStatSlots
+  int32_t* fb_ctrl;  // [0] count, [1] head
+  int32_t* fb_list;
+  float* slab_s;
+  int32_t* slab_i;
+  float* samp;
+  float* scratch;
+};
+
+enum StatSlot { kStatStoreAll = 0, kStatSampled, kStatFallback, kStatMax, kStatMin, kStatTotal, kStatSlots = 8 };
+
+hipError_t launch_score_store(const DevProblem& P, float* out, int64_t ld, hipStream_t s);
+hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_idx, hipStream_t s);
+
+hipError_t launch_select_single(const float* x, int64_t ld, const int32_t* row_start, const int32_t* len,
+                                int32_t rows, int32_t k, int32_t* out, hipStream_t s);
+hipError_t launch_select_split(const float* x, int64_t ld, const int32_t* row_start, const int32_t* len,
+                               int32_t rows, int32_t k, int32_t g, int32_t* out, void* ws, hipStream_t s);
+size_t select_split_ws_bytes(int32_t rows);
+
+// Score-kernel work decomposition shared with the host sizing code.
+int rows_per_block(int heads);
+int sample_stride_for(int k);  // odd stride S
+
+}  // namespace idx

@@ -1,0 +1,201 @@
+// Exact top-k over materialised fp32 rows (idx_select), gfx950.
+//
+// ROCm DSA indexer top-k page (sgl-project/sglang#37591): fp32 radix histogram of 12
+// bits, exact tie refinement, full-row rescan when the tie buffer overflows, and, for
+// long rows at low batch, several workgroups per row ("row split"):
+//   split == 0  select_rows_kernel: one 1024-thread workgroup per row (block_select)
+//   split >= 2  mb_hist_kernel    g workgroups per row add their segment's level-1
+//                                 histogram into a per-row global histogram
+//               mb_scatter_kernel every workgroup finds the boundary bin from it, writes
+//                                 its elements above the bin to the output and appends
+//                                 the bin's elements to a per-row tie buffer
+//               mb_refine_kernel  one workgroup per row refines the tie buffer in LDS,
+//                                 or reruns the whole row in rescan mode if it overflowed
+#include "launch.hpp"
+#include "select_core.hpp"
+
+namespace idx {
+
+constexpr int kSelThreads = 1024;
+
+__global__ __launch_bounds__(kSelThreads) void select_rows_kernel(const float* x, int64_t ld,
+                                                                  const int32_t* row_start, const int32_t* len,
+                                                                  int32_t k, int32_t* out) {
+  __shared__ SelSmem sm;
+  const int r = blockIdx.x;
+  const int n = len[r];
+  const int64_t off = (int64_t)r * ld + (row_start ? row_start[r] : 0);
+  const int m = min(k, n);
+  int32_t* o = out + (int64_t)r * k;
+  if (m > 0) block_select<kSelThreads>(RowSrc{x + off}, n, m, o, sm);
+  for (int j = m + threadIdx.x; j < k; j += kSelThreads) o[j] = -1;
+}
+
+struct SplitWs {
+  uint32_t* hist;  // [rows][4096]
+  int32_t* pos;    // [rows] output cursor
+  int32_t* tcnt;   // [rows] tie count
+  uint32_t* tkey;  // [rows][kTieCap]
+  int32_t* tidx;   // [rows][kTieCap]
+};
+
+static SplitWs carve(void* ws, int rows) {
+  SplitWs W;
+  char* p = static_cast<char*>(ws);
+  W.hist = reinterpret_cast<uint32_t*>(p);
+  p += (size_t)rows * kHistBins * 4;
+  W.pos = reinterpret_cast<int32_t*>(p);
+  p += (size_t)rows * 4;
+  W.tcnt = reinterpret_cast<int32_t*>(p);
+  p += (size_t)rows * 4;
+  p = reinterpret_cast<char*>(((uintptr_t)p + 255) & ~(uintptr_t)255);
+  W.tkey = reinterpret_cast<uint32_t*>(p);
+  p += (size_t)rows * kTieCap * 4;
+  W.tidx = reinterpret_cast<int32_t*>(p);
+  return W;
+}
+
+size_t select_split_ws_bytes(int32_t rows) {
+  size_t b = (size_t)rows * kHistBins * 4 + (size_t)rows * 8;
+  b = (b + 255) & ~(size_t)255;
+  b += (size_t)rows * kTieCap * 8;
+  return b + 256;
+}
+
+// Clears hist, pos and tcnt (contiguous at the start of the workspace).
+__global__ void zero_words_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+__device__ __forceinline__ void segment(int n, int g, int part, int& lo, int& hi) {
+  const int seg = (n + g - 1) / g;
+  lo = min(n, part * seg);
+  hi = min(n, lo + seg);
+}
+
+__global__ __launch_bounds__(kSelThreads) void mb_hist_kernel(const float* x, int64_t ld, const int32_t* row_start,
+                                                              const int32_t* len, int32_t k, int32_t g, SplitWs W) {
+  __shared__ SelSmem sm;
+  const int r = blockIdx.x / g, part = blockIdx.x % g;
+  const int n = len[r];
+  if (min(k, n) >= n) return;  // the refine kernel writes trivial rows
+  int lo, hi;
+  segment(n, g, part, lo, hi);
+  zero_hist<kSelThreads>(sm, kHistBins);
+  __syncthreads();
+  const int64_t off = (int64_t)r * ld + (row_start ? row_start[r] : 0) + lo;
+  hist_level1<kSelThreads>(RowSrc{x + off}, hi - lo, sm);
+  __syncthreads();
+  uint32_t* gh = W.hist + (int64_t)r * kHistBins;
+  for (int b = threadIdx.x; b < kHistBins; b += kSelThreads)
+    if (sm.hist[b]) atomicAdd(&gh[b], sm.hist[b]);
+}
+
+__device__ __forceinline__ void load_row_hist(SelSmem& sm, const uint32_t* gh) {
+  for (int b = threadIdx.x; b < kHistBins; b += kSelThreads) sm.hist[b] = gh[b];
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kSelThreads) void mb_scatter_kernel(const float* x, int64_t ld,
+                                                                 const int32_t* row_start, const int32_t* len,
+                                                                 int32_t k, int32_t g, int32_t* out, SplitWs W) {
+  __shared__ SelSmem sm;
+  const int r = blockIdx.x / g, part = blockIdx.x % g;
+  const int n = len[r];
+  const int m = min(k, n);
+  if (m >= n) return;
+  load_row_hist(sm, W.hist + (int64_t)r * kHistBins);
+  find_boundary<kSelThreads>(sm, kHistBins, (uint32_t)m);
+  const uint32_t b1 = (uint32_t)sm.bnd_bin;
+  const uint32_t cnt = sm.bnd_count;
+  const bool all_bin = cnt == (uint32_t)m - sm.bnd_above;
+  const bool keep_ties = !all_bin && cnt <= (uint32_t)kTieCap;
+  int lo, hi;
+  segment(n, g, part, lo, hi);
+  const int64_t off = (int64_t)r * ld + (row_start ? row_start[r] : 0);
+  int32_t* o = out + (int64_t)r * k;
+  for (int base = lo; base < hi; base += kSelThreads) {
+    const int j = base + (int)threadIdx.x;
+    uint32_t key = 0, d = 0;
+    if (j < hi) {
+      key = order_key(x[off + j]);
+      d = key >> (32 - kHistBits);
+    }
+    const bool emit = j < hi && (d > b1 || (all_bin && d == b1));
+    const bool tie = j < hi && keep_ties && d == b1;
+    const int so = wave_append_slot(emit, &W.pos[r]);
+    if (emit) o[so] = j;
+    const int st = wave_append_slot(tie, &W.tcnt[r]);
+    if (tie) {
+      W.tkey[(int64_t)r * kTieCap + st] = key;
+      W.tidx[(int64_t)r * kTieCap + st] = j;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads) void mb_refine_kernel(const float* x, int64_t ld,
+                                                                const int32_t* row_start, const int32_t* len,
+                                                                int32_t k, int32_t* out, SplitWs W) {
+  __shared__ SelSmem sm;
+  const int r = blockIdx.x;
+  const int n = len[r];
+  const int m = min(k, n);
+  int32_t* o = out + (int64_t)r * k;
+  const int64_t off = (int64_t)r * ld + (row_start ? row_start[r] : 0);
+  if (m >= n) {
+    for (int j = threadIdx.x; j < n; j += kSelThreads) o[j] = j;
+  } else {
+    load_row_hist(sm, W.hist + (int64_t)r * kHistBins);
+    find_boundary<kSelThreads>(sm, kHistBins, (uint32_t)m);
+    const uint32_t above = sm.bnd_above;
+    const uint32_t cnt = sm.bnd_count;
+    const uint32_t need = (uint32_t)m - above;
+    __syncthreads();
+    if (cnt == need) {
+      // every element of the boundary bin was emitted by the scatter kernel
+    } else if (cnt <= (uint32_t)kTieCap) {
+      for (int t = threadIdx.x; t < (int)cnt; t += kSelThreads) {
+        sm.tkey[t] = W.tkey[(int64_t)r * kTieCap + t];
+        sm.tidx[t] = W.tidx[(int64_t)r * kTieCap + t];
+      }
+      if (threadIdx.x == 0) {
+        sm.ntie = (int)cnt;
+        sm.nout = (int)above;
+      }
+      __syncthreads();
+      refine_lds<kSelThreads>(2, need, o, sm);
+    } else {
+      // tie buffer overflow: redo the whole row in one workgroup (rescan mode)
+      block_select<kSelThreads>(RowSrc{x + off}, n, m, o, sm);
+    }
+  }
+  for (int j = m + threadIdx.x; j < k; j += kSelThreads) o[j] = -1;
+}
+
+hipError_t launch_select_single(const float* x, int64_t ld, const int32_t* row_start, const int32_t* len,
+                                int32_t rows, int32_t k, int32_t* out, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  select_rows_kernel<<<dim3(rows), dim3(kSelThreads), 0, s>>>(x, ld, row_start, len, k, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_split(const float* x, int64_t ld, const int32_t* row_start, const int32_t* len,
+                               int32_t rows, int32_t k, int32_t g, int32_t* out, void* ws, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const SplitWs W = carve(ws, rows);
+  const int64_t zero_words = (int64_t)rows * (kHistBins + 2);
+  const int64_t zb = (zero_words + 255) / 256;
+  zero_words_kernel<<<dim3((unsigned)(zb < 1024 ? zb : 1024)), dim3(256), 0, s>>>(W.hist, zero_words);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((int64_t)rows * g)), block(kSelThreads);
+  mb_hist_kernel<<<grid, block, 0, s>>>(x, ld, row_start, len, k, g, W);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  mb_scatter_kernel<<<grid, block, 0, s>>>(x, ld, row_start, len, k, g, out, W);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  mb_refine_kernel<<<dim3(rows), block, 0, s>>>(x, ld, row_start, len, k, out, W);
+  return hipGetLastError();
+}
+
+}  // namespace idx
