@@ -1,0 +1,193 @@
+#!/usr/bin/env python
+"""Benchmark of the fused no-logits DSA indexer top-k on one MI355X.
+
+One step = one idx_fused_topk call over the whole batch: threshold samples, thresholds,
+fused score + filter into the candidate slab, slab select and the exact fallback.  The
+default workload is the long-context prefill: 4096 rows x 1,048,576 keys (causal,
+offset 1,044,480), 32 heads, head_dim 128, MXFP4 q/k, k = 2048.  Inputs are synthetic,
+seeded, and resident in HBM before the timed region starts.
+
+Prints exactly one JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload long|prefill|decode|tiny]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"mxfp4": 10100.0, "e4m3": 5000.0}   # MI355X dense MFMA peaks
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["fused.hip", "score_core.hpp", "common.hpp"]
+
+WORKLOADS = {
+    "long": "long-context prefill: 4096 rows x 1,048,576 keys, causal offset 1,044,480, 32 heads, MXFP4, k=2048",
+    "prefill": "prefill: 4096 rows x 65,536 keys, causal offset 61,440, 64 heads, e4m3 + per-key scale, k=2048",
+    "decode": "decode/MTP: 128 requests x 4 rows, paged K (64-token pages), context 8K-256K, 64 heads, e4m3, k=2048",
+    "tiny": "tiny: 64 rows x 4096 keys, 32 heads, integer e4m3, k=512",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "sparse_attention_indexer_score_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload, launch_bytes_alg):
+    """HBM bytes of one fused score+filter launch from committed rocprofv3 counter runs,
+    or None when they are missing or were taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"score_filter_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(p, rows_sample):
+    """The oracle as it stands, timed on the host cores over a bounded sample of rows."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    oracle.topk(p, rows=rows_sample)
+    dt = time.perf_counter() - t0
+    pairs = int(sum(int(p.ke[r]) - int(p.ks[r]) for r in rows_sample))
+    return {"value": pairs / dt / 1e9, "unit": "Gkey-scores/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(rows_sample)} of {p.rows} rows (every {p.rows // len(rows_sample)}th), all their "
+                      f"visible keys ({pairs} key-scores), scoring + full sort; includes one decode of K; "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-rows", type=int, default=16, help="rows in the oracle's timed sample (0: skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (reference kernel for HBM counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (rows shard with no "
+              "communication; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_attention_indexer_score_amd as sai
+    from sparse_attention_indexer_score_amd import workloads as wl
+
+    log(f"[bench] generating workload '{args.workload}'")
+    t = time.perf_counter()
+    p = wl.make(args.workload)
+    log(f"[bench] generated in {time.perf_counter() - t:.1f}s: rows={p.rows} pairs={p.pairs}")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dp = sai.DeviceProblem.from_host(p, dev)
+    k = p.topk
+    runner = sai.FusedRunner(dp, k)
+    torch.cuda.synchronize()
+    log(f"[bench] resident; workspace {runner.nbytes / 2**20:.0f} MiB")
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+        log("[bench] copy calibration kernel done (1 GiB read + 1 GiB write)")
+
+    _, st = runner(stats=True)
+    torch.cuda.synchronize()
+    log(f"[bench] route: {st}")
+    for _ in range(max(0, args.warmup - 1)):
+        runner()
+    torch.cuda.synchronize()
+
+    sai.idx_timing_enable(args.steps)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        runner()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stages = sai.idx_timing_read(args.steps)
+    sai.idx_timing_disable()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] {args.steps} steps: {ms:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f} ms/step)")
+
+    stage_ms = {s: float(np.mean([c[s] for c in stages])) for s in sai.FUSED_STAGES}
+    pairs = p.pairs
+    value = pairs / (ms * 1e-3) / 1e9
+    flops_per_pair = 2 * 128 * p.heads
+    alg_flops = pairs * flops_per_pair                    # one fused score+filter launch
+    k2_ms = stage_ms["score_filter"]
+    achieved = alg_flops / (k2_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[p.fmt]
+    traffic = load_traffic(args.workload, None)
+
+    cpu = None
+    if args.cpu_rows > 0:
+        step = max(1, p.rows // args.cpu_rows)
+        rows_sample = list(range(0, p.rows, step))[:args.cpu_rows]
+        log(f"[bench] timing the CPU oracle on {len(rows_sample)} rows")
+        cpu = cpu_baseline(p, rows_sample)
+        log(f"[bench] cpu baseline {cpu['value']:.5f} Gkey-scores/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": "indexer Gkey-scores/s + fused top-k ms (4096 rows x 1M keys, k=2048), 1 GPU",
+        "value": round(value, 3),
+        "unit": "Gkey-scores/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "fused_topk_ms": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.fmt,
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.workload], "rows": p.rows, "key_scores": pairs, "k": k,
+                   "heads": p.heads, "head_dim": 128, "format": p.fmt},
+        "roofline": {"bound": "mfma", "kernel": "score_kernel (fused score + filter)",
+                     "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "alg_flops_per_launch": alg_flops, "launch_ms": round(k2_ms, 4)},
+        "stage_ms": {s: round(v, 4) for s, v in stage_ms.items()},
+        "route": {kk: st[kk] for kk in ("rows_store_all", "rows_sampled", "fallback_rows", "max_count",
+                                         "min_count", "total_count", "cap", "sample_stride")},
+        "logits_bytes_avoided": int(pairs) * 4 * 2,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -182,6 +182,19 @@ int idx_fused_topk(const idx_problem* p, int32_t k, int32_t* out_idx, void* ws, 
  * reads only the scalar fields of p).  Returns 0 for invalid arguments.            */
 size_t idx_fused_workspace(const idx_problem* p, int32_t k);
 
+/* ------------------------------------------------------------------ measurement
+ * Stage timing of idx_fused_topk for benchmarks.  While enabled, every idx_fused_topk
+ * call (any thread) records six HIP events on its own stream at its stage boundaries,
+ * without synchronising; the records of up to max_calls calls are kept (later calls are
+ * not timed).  idx_timing_read waits for the recorded events and writes, per timed call,
+ * the milliseconds of the five stages in order — threshold samples, thresholds, fused
+ * score + filter, slab select, fallback — to ms (host, [calls][5]); it returns the number
+ * of calls written (<= max_calls) or a negative error code, and starts a new record.
+ * idx_timing_disable stops recording and releases the events.                       */
+int idx_timing_enable(int32_t max_calls);
+int idx_timing_read(float* ms, int32_t max_calls);
+int idx_timing_disable(void);
+
 /* ------------------------------------------------------------------ misc */
 const char* idx_strerror(int code);
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */

@@ -149,8 +149,14 @@ def dequant_keys(p, phys: np.ndarray) -> np.ndarray:
 
 
 def all_keys(p) -> np.ndarray:
-    """Every key of a contiguous problem, decoded once: float64 [num_keys, 128]."""
-    return dequant_keys(p, np.arange(p.num_keys, dtype=np.int64))
+    """Every key of a contiguous problem, decoded once: float64 [num_keys, 128]
+    (in slices of 16384 keys, which only bounds the size of the temporaries)."""
+    out = np.empty((p.num_keys, HEAD_DIM), dtype=np.float64)
+    step = 1 << 14
+    for i in range(0, p.num_keys, step):
+        j = min(p.num_keys, i + step)
+        out[i:j] = dequant_keys(p, np.arange(i, j, dtype=np.int64))
+    return out
 
 
 def row_scores(p, r: int, qd=None, kd_all=None) -> np.ndarray:

@@ -80,6 +80,9 @@ def _lib():
             "idx_fused_workspace": (sz, [P, i32]),
             "idx_strerror": (ctypes.c_char_p, [ctypes.c_int]),
             "idx_version": (i32, []),
+            "idx_timing_enable": (ctypes.c_int, [i32]),
+            "idx_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float), i32]),
+            "idx_timing_disable": (ctypes.c_int, []),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)
@@ -260,3 +263,23 @@ def idx_fused_topk(prob: DeviceProblem, k: int, stats: bool = False, stream=None
 
 def version() -> int:
     return int(_lib().idx_version())
+
+
+FUSED_STAGES = ("sample", "threshold", "score_filter", "slab_select", "fallback")
+
+
+def idx_timing_enable(max_calls: int):
+    _check(_lib().idx_timing_enable(max_calls), "idx_timing_enable")
+
+
+def idx_timing_read(max_calls: int):
+    """Per timed idx_fused_topk call, the milliseconds of its five stages (list of dicts)."""
+    buf = (ctypes.c_float * (5 * max_calls))()
+    n = _lib().idx_timing_read(buf, max_calls)
+    if n < 0:
+        raise IdxError(n, "idx_timing_read")
+    return [dict(zip(FUSED_STAGES, buf[5 * c:5 * c + 5])) for c in range(n)]
+
+
+def idx_timing_disable():
+    _check(_lib().idx_timing_disable(), "idx_timing_disable")

@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "../../include/idx.h"
 #include "launch.hpp"
@@ -135,6 +136,24 @@ FusedSizes fused_sizes(const idx_problem* p, int32_t k) {
 
 int hip_err(hipError_t e) { return e == hipSuccess ? IDX_OK : IDX_EHIP; }
 
+// Stage timing record (idx_timing_*): 6 events per timed call.
+constexpr int kStageEvents = 6;
+struct Timing {
+  bool on = false;
+  int max_calls = 0;
+  int used = 0;
+  std::vector<hipEvent_t> ev;
+};
+Timing g_timing;
+std::mutex g_timing_mu;
+
+// Events for the next timed call, or nullptr.
+hipEvent_t* next_timing_slot() {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  if (!g_timing.on || g_timing.used >= g_timing.max_calls) return nullptr;
+  return &g_timing.ev[(size_t)(g_timing.used++) * kStageEvents];
+}
+
 int check_select(const float* scores, int64_t ld, const int32_t* len, int32_t rows, int32_t k, int32_t* out) {
   if (rows < 0 || k < 1 || k > IDX_MAX_TOPK || ld < 0 || ld > INT32_MAX) return IDX_EINVAL;
   if (rows > 0 && (!scores || !len || !out)) return IDX_EINVAL;
@@ -264,7 +283,7 @@ int idx_fused_topk(const idx_problem* p, int32_t k, int32_t* out_idx, void* ws, 
   F.samp = reinterpret_cast<float*>(base + z.off_samp);
   F.scratch = reinterpret_cast<float*>(base + z.off_scratch);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((rc = hip_err(launch_fused(P, F, out_idx, s)))) return rc;
+  if ((rc = hip_err(launch_fused(P, F, out_idx, s, next_timing_slot())))) return rc;
   if (stats) {
     long long h[kStatSlots];
     if (hipMemcpyAsync(h, F.stats, sizeof(h), hipMemcpyDeviceToHost, s) != hipSuccess) return IDX_EHIP;
@@ -277,6 +296,45 @@ int idx_fused_topk(const idx_problem* p, int32_t k, int32_t* out_idx, void* ws, 
     stats->total_count = h[kStatTotal];
   }
   return IDX_OK;
+}
+
+int idx_timing_disable(void) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  for (hipEvent_t e : g_timing.ev) (void)hipEventDestroy(e);
+  g_timing = Timing();
+  return IDX_OK;
+}
+
+int idx_timing_enable(int32_t max_calls) {
+  if (max_calls < 1 || max_calls > (1 << 20)) return IDX_EINVAL;
+  idx_timing_disable();
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  g_timing.ev.resize((size_t)max_calls * kStageEvents, nullptr);
+  for (auto& e : g_timing.ev) {
+    if (hipEventCreate(&e) != hipSuccess) {
+      e = nullptr;
+      return IDX_EHIP;
+    }
+  }
+  g_timing.max_calls = max_calls;
+  g_timing.used = 0;
+  g_timing.on = true;
+  return IDX_OK;
+}
+
+int idx_timing_read(float* ms, int32_t max_calls) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  if (!g_timing.on) return IDX_EINVAL;
+  if (!ms || max_calls < 0) return IDX_EINVAL;
+  const int n = std::min(g_timing.used, max_calls);
+  for (int c = 0; c < n; ++c) {
+    hipEvent_t* e = &g_timing.ev[(size_t)c * kStageEvents];
+    if (hipEventSynchronize(e[kStageEvents - 1]) != hipSuccess) return IDX_EHIP;
+    for (int i = 0; i + 1 < kStageEvents; ++i)
+      if (hipEventElapsedTime(&ms[c * (kStageEvents - 1) + i], e[i], e[i + 1]) != hipSuccess) return IDX_EHIP;
+  }
+  g_timing.used = 0;
+  return n;
 }
 
 }  // extern "C"

@@ -417,9 +417,11 @@ hipError_t launch_score_store(const DevProblem& P, float* out, int64_t ld, hipSt
   return dispatch_score<MODE_STORE>(P, E, tile_work(P.rows, P.heads, P.key_span, kChunkKeys), s);
 }
 
-hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_idx, hipStream_t s) {
+hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_idx, hipStream_t s, hipEvent_t* ev) {
   if (P.rows == 0) return hipSuccess;
   hipError_t e;
+  auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
+  if ((e = mark(0)) != hipSuccess) return e;
   // K1a: samples
   {
     EpiArgs E = {};
@@ -430,6 +432,7 @@ hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_id
     if (F.debug_mode != 0 && F.debug_row_mod <= 0) E.skip_le = 0x7FFFFFFF;  // every row forced
     if ((e = dispatch_score<MODE_SAMPLE>(P, E, tile_work(P.rows, P.heads, F.ns, kChunkSamples), s)) != hipSuccess)
       return e;
+    if ((e = mark(1)) != hipSuccess) return e;
   }
   // K1b: thresholds (also clears counts, stats and the fallback queue)
   {
@@ -451,6 +454,7 @@ hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_id
     T.debug_row_mod = F.debug_row_mod;
     threshold_kernel<<<dim3(P.rows), dim3(kThreads), 0, s>>>(T);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = mark(2)) != hipSuccess) return e;
   }
   // K2: fused score + filter
   {
@@ -462,6 +466,7 @@ hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_id
     E.cap = F.cap;
     if ((e = dispatch_score<MODE_FILTER>(P, E, tile_work(P.rows, P.heads, P.key_span, kChunkKeys), s)) != hipSuccess)
       return e;
+    if ((e = mark(3)) != hipSuccess) return e;
   }
   // K3: select over the slab
   {
@@ -479,6 +484,7 @@ hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_id
     S.cap = F.cap;
     slab_select_kernel<<<dim3(P.rows), dim3(kThreads), 0, s>>>(S);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = mark(4)) != hipSuccess) return e;
   }
   // K4: exact fallback for queued rows (exits at once when the queue is empty)
   {
@@ -499,6 +505,7 @@ hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_id
       else fallback_kernel<FMT_MXFP4, 32><<<grid, block, 0, s>>>(A, B);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = mark(5)) != hipSuccess) return e;
   }
   return hipSuccess;
 }

@@ -44,7 +44,9 @@ struct FusedPlan {
 enum StatSlot { kStatStoreAll = 0, kStatSampled, kStatFallback, kStatMax, kStatMin, kStatTotal, kStatSlots = 8 };
 
 hipError_t launch_score_store(const DevProblem& P, float* out, int64_t ld, hipStream_t s);
-hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_idx, hipStream_t s);
+// ev: optional 6 events recorded at the stage boundaries (before K1a .. after K4).
+hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_idx, hipStream_t s,
+                        hipEvent_t* ev = nullptr);
 
 hipError_t launch_select_single(const float* x, int64_t ld, const int32_t* row_start, const int32_t* len,
                                 int32_t rows, int32_t k, int32_t* out, hipStream_t s);

@@ -122,26 +122,14 @@ def encode_bf16(x: np.ndarray) -> np.ndarray:
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
 
 
-# e2m1 codes 0..7 in magnitude order: 0, 0.5, 1, 1.5, 2, 3, 4, 6.  Values between two grid
-# points go to the nearer one; exact midpoints go to the code with an even mantissa bit.
-_E2M1_EDGES = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], dtype=np.float64)
-_E2M1_TIE_UP = np.array([False, True, False, True, False, True, False])
-
-
+# e2m1 codes 0..7 in magnitude order: 0, 0.5, 1, 1.5, 2, 3, 4, 6.  A magnitude maps to the
+# nearer grid point; an exact midpoint goes to the neighbour whose mantissa bit is 0 (ties
+# to even), which is why some edges below are strict (>) and others inclusive (>=).
 def _e2m1_codes(y: np.ndarray) -> np.ndarray:
     a = np.abs(y)
-    code = np.searchsorted(_E2M1_EDGES, a, side="left").astype(np.uint8)
-    # a value exactly on an edge sits at index i (side='left'); move it up when the tie
-    # resolves to the upper neighbour (whose mantissa bit is even).
-    on_edge = np.zeros(a.shape, dtype=bool)
-    inb = code < len(_E2M1_EDGES)
-    on_edge[inb] = a[inb] == _E2M1_EDGES[code[inb]]
-    up = np.zeros(a.shape, dtype=bool)
-    up[on_edge] = _E2M1_TIE_UP[code[on_edge]]
-    code = code + up.astype(np.uint8)
-    code = np.minimum(code, 7)
-    sign = (np.signbit(y)).astype(np.uint8) << 3
-    return code | sign
+    code = ((a > 0.25).astype(np.uint8) + (a >= 0.75) + (a > 1.25) + (a >= 1.75)
+            + (a > 2.5) + (a >= 3.5) + (a > 5.0)).astype(np.uint8)
+    return code | (np.signbit(y).astype(np.uint8) << 3)
 
 
 def encode_mxfp4(x: np.ndarray):
@@ -154,12 +142,12 @@ def encode_mxfp4(x: np.ndarray):
     x = np.asarray(x, dtype=np.float32)
     assert x.shape[-1] == HEAD_DIM
     lead = x.shape[:-1]
-    xb = x.reshape(*lead, 4, 32).astype(np.float64)
+    xb = x.reshape(*lead, 4, 32)
     amax = np.max(np.abs(xb), axis=-1)
-    with np.errstate(divide="ignore"):
-        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
+    _, ex = np.frexp(amax)                      # amax = m * 2^ex, m in [0.5, 1): floor(log2) = ex - 1
+    e = np.where(amax > 0, ex.astype(np.int32) - 1 - 2, -127)
     e = np.clip(e, -127, 127).astype(np.int32)
-    y = xb / np.exp2(e.astype(np.float64))[..., None]
+    y = np.ldexp(xb, (-e)[..., None].astype(np.int32)).astype(np.float32)   # exact power-of-two scaling
     codes = _e2m1_codes(y).reshape(*lead, HEAD_DIM)
     packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
     sf = (e + 127).astype(np.uint8)
@@ -221,9 +209,12 @@ def long_context(rows=4096, num_keys=1 << 20, heads=32, topk=2048, seed=4, band_
     rq, rk, ru, rp, rw = _streams(seed, 5)
     u = ru.standard_normal(HEAD_DIM)
     u = (u / np.linalg.norm(u)).astype(np.float32)
-    qf = rq.standard_normal((rows, heads, HEAD_DIM), dtype=np.float32) + 2.0 * u
-    q, q_sf = encode_mxfp4(qf)
-    del qf
+    q = np.empty((rows, heads, HEAD_DIM // 2), dtype=np.uint8)
+    q_sf = np.empty((rows, heads, 4), dtype=np.uint8)
+    for i in range(0, rows, 512):
+        m = min(512, rows - i)
+        qf = rq.standard_normal((m, heads, HEAD_DIM), dtype=np.float32) + 2.0 * u
+        q[i:i + m], q_sf[i:i + m] = encode_mxfp4(qf)
     ks, ke = _causal(rows, num_keys)
     common = int(ke.min())                       # keys [0, common) are visible to every row
     target = band_keys if band_keys is not None else 2 * topk
