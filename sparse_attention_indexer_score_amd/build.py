@@ -29,6 +29,8 @@ COMMON = [
 DEVICE = [
     "--offload-arch=gfx950",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the head reduce reads them directly (no v_accvgpr_read)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

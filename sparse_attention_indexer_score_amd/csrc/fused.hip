@@ -27,7 +27,17 @@ enum : int { MODE_STORE = 0, MODE_FILTER = 1, MODE_SAMPLE = 2 };
 constexpr int kThreads = 256;  // 4 waves per workgroup
 constexpr int kTile = 32;      // keys per MFMA block
 
-int rows_per_block(int heads) { return 4 * (heads == 64 ? 2 : 4); }
+#ifndef IDX_ROWS_PER_WAVE
+#define IDX_ROWS_PER_WAVE 2
+#endif
+constexpr int kRowsPerWave = IDX_ROWS_PER_WAVE;  // rows per wave of the contiguous-K kernel
+
+// Rows per workgroup of the paged kernel (score_kernel) and of score_tiles_kernel.
+static int rows_per_block_paged(int heads) { return 4 * (heads == 64 ? 2 : 4); }
+int rows_per_block(int heads) { return 4 * kRowsPerWave; }
+static int rows_per_block_for(const DevProblem& P) {
+  return P.page_table ? rows_per_block_paged(P.heads) : rows_per_block(P.heads);
+}
 
 // Odd sample stride: the largest odd S <= 2.25*k/64, so that a row of V keys yields about
 // V/S samples of which m ~ 64 lie at or above the threshold (LiteTopK page, section 2:
@@ -213,6 +223,199 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs A, EpiArgs E,
   }
 }
 
+// Contiguous-K scoring kernel (STORE / FILTER / SAMPLE epilogues).
+//
+// Every row of a workgroup reads the same keys, so a wave holds RW rows' query operands in
+// registers and streams 32-key tiles: the tile's key operand is loaded once per wave
+// (scalar tile base + per-lane offset, next tile prefetched) and multiplied against all RW
+// rows.  Row ranges are wave-uniform and kept in scalar registers; a tile that lies inside
+// every row's range takes a branch-free path that issues all MFMAs before the head-reduce
+// VALU work, so the reduce of one row overlaps the MFMAs of the next.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+template <int FMT>
+__device__ __forceinline__ void load_key_at(KeyOperand& ko, const uint8_t* kbase, const uint8_t* sfbase,
+                                            uint32_t off, uint32_t sf_off) {
+  constexpr int KB = Fmt<FMT>::kBytes;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    if constexpr (FMT == FMT_E4M3) {
+      const v4i x0 = *reinterpret_cast<const v4i*>(kbase + off + ks * (KB / 2));
+      const v4i x1 = *reinterpret_cast<const v4i*>(kbase + off + ks * (KB / 2) + 16);
+      ko.b[ks] = v8i{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      ko.sb[ks] = 127;
+    } else {
+      const v4i x = *reinterpret_cast<const v4i*>(kbase + off + ks * (KB / 2));
+      ko.b[ks] = v8i{x.x, x.y, x.z, x.w, 0, 0, 0, 0};
+    }
+  }
+  if constexpr (FMT == FMT_MXFP4) {
+    const int half = lane_id() >> 5;
+    const uint32_t sw = *reinterpret_cast<const uint32_t*>(sfbase + sf_off);
+    ko.sb[0] = (sw >> (8 * half)) & 0xFF;
+    ko.sb[1] = (sw >> (8 * (2 + half))) & 0xFF;
+  }
+}
+
+template <int FMT, int H>
+__device__ __forceinline__ void mfma_row(v16f (&acc)[H / 32], const RowOperand<FMT, H>& ro, const KeyOperand& ko) {
+  constexpr int C = Fmt<FMT>::kCode;
+#pragma unroll
+  for (int mt = 0; mt < H / 32; ++mt) {
+    v16f a = {};
+    a = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ro.a[mt][0], ko.b[0], a, C, C, 0, ro.sa[mt][0], 0, ko.sb[0]);
+    a = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ro.a[mt][1], ko.b[1], a, C, C, 0, ro.sa[mt][1], 0, ko.sb[1]);
+    acc[mt] = a;
+  }
+}
+
+// Same arithmetic, in the same order, as row_partial().
+template <int FMT, int H>
+__device__ __forceinline__ float reduce_row(const v16f (&acc)[H / 32], const RowOperand<FMT, H>& ro) {
+  float p = 0.0f;
+#pragma unroll
+  for (int mt = 0; mt < H / 32; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p = __builtin_fmaf(ro.w[mt][i], relu(acc[mt][i]), p);
+  return p;
+}
+
+template <int FMT, int H, int MODE, int RW>
+__global__ __launch_bounds__(kThreads) void score_tiles_kernel(ScoreArgs A, EpiArgs E, TileWork W) {
+  static_assert(RW % 2 == 0, "rows are processed in pairs");
+  constexpr int KB = Fmt<FMT>::kBytes;
+  constexpr int RB = 4 * RW;
+  constexpr int NP = RW / 2;
+  const int64_t item = map_item(W);
+  if (item >= W.total) return;
+  const int rb = (int)(item % W.nrb);
+  const int chunk = (int)(item / W.nrb);
+  const int wave = uniform(threadIdx.x / kWave);
+  const int l = lane_id();
+  const int half = l >> 5, col = l & 31;
+  const int row0 = rb * RB + wave * RW;
+  const int S = (MODE == MODE_SAMPLE) ? E.stride : 1;
+  const int phase = (MODE == MODE_SAMPLE) ? sample_phase(rb, S) : 0;
+
+  // Row ranges in position space (keys, or sample slots), wave-uniform.
+  int plo[RW], phi[RW], ksr[RW];
+  int wlo = 0x7FFFFFFF, whi = 0, full_lo = 0, full_hi = 0x7FFFFFFF;
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    const int r = row0 + i;
+    plo[i] = phi[i] = ksr[i] = 0;
+    if (r < A.rows) {
+      const int ks = uniform(A.ks[r]), ke = uniform(A.ke[r]);
+      ksr[i] = ks;
+      if (MODE == MODE_SAMPLE) {
+        if (ke - ks > E.skip_le) sample_range(ks, ke, phase, S, plo[i], phi[i]);
+      } else {
+        plo[i] = ks;
+        phi[i] = ke;
+      }
+    }
+    if (phi[i] > plo[i]) {
+      wlo = min(wlo, plo[i]);
+      whi = max(whi, phi[i]);
+    }
+    full_lo = max(full_lo, plo[i]);
+    full_hi = min(full_hi, phi[i]);
+  }
+  const int c0 = chunk * W.chunk, c1 = c0 + W.chunk;
+  const int t0 = max(c0, wlo) / kTile, t1 = (min(c1, whi) + kTile - 1) / kTile;
+  if (t0 >= t1) return;
+
+  RowOperand<FMT, H> ro[RW];
+#pragma unroll
+  for (int i = 0; i < RW; ++i)
+    if (row0 + i < A.rows) load_row<FMT, H>(ro[i], A, row0 + i);
+
+  // Per-lane constants of each row pair: lanes 0-31 carry row 2p, lanes 32-63 row 2p+1.
+  float thr_l[NP];
+  int ks_l[NP], lo_l[NP], hi_l[NP];
+  int64_t row_l[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int i = 2 * p + half;
+    row_l[p] = row0 + i;
+    ks_l[p] = half ? ksr[2 * p + 1] : ksr[2 * p];
+    lo_l[p] = half ? plo[2 * p + 1] : plo[2 * p];
+    hi_l[p] = half ? phi[2 * p + 1] : phi[2 * p];
+    thr_l[p] = 0.0f;
+    if (MODE == MODE_FILTER && row0 + i < A.rows) thr_l[p] = E.thr[row0 + i];
+  }
+
+  const int64_t kstep = (int64_t)kTile * S;                 // keys per tile
+  const uint32_t off = (uint32_t)(col * S) * KB + half * (KB / 4);
+  const uint32_t sf_off = (uint32_t)(col * S) * 4;
+  const int64_t last_key = A.num_keys - 1;
+  auto tile_key0 = [&](int t) -> int64_t { return (int64_t)phase + (int64_t)t * kstep; };
+  auto load_tile = [&](KeyOperand& ko, int t) {
+    const int64_t k0 = tile_key0(t);
+    if (k0 + (kTile - 1) * (int64_t)S <= last_key) {
+      load_key_at<FMT>(ko, A.k + k0 * KB, A.k_sf + k0 * 4, off, sf_off);
+    } else {  // ragged tail: clamp every lane to a real key (results are masked)
+      int64_t key = k0 + (int64_t)col * S;
+      key = key < last_key ? key : last_key;
+      load_key_at<FMT>(ko, A.k + key * KB, A.k_sf + key * 4, half * (KB / 4), 0);
+    }
+  };
+
+  // One tile: MFMAs for all RW rows first, then the head reduce and epilogue per row pair.
+  // Rows that do not see (part of) the tile are computed anyway and masked per lane.
+  auto compute = [&](const KeyOperand& kc, int t) {
+    const int pos = t * kTile + col;
+    const int64_t key = tile_key0(t) + (int64_t)col * S;
+    const bool full = t * kTile >= full_lo && (t + 1) * kTile <= full_hi;  // wave-uniform
+    float kscale = 1.0f;
+    if (A.k_scale) kscale = A.k_scale[key < last_key ? key : last_key];
+    v16f acc[RW][H / 32];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) mfma_row<FMT, H>(acc[i], ro[i], kc);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const float pa = reduce_row<FMT, H>(acc[2 * p], ro[2 * p]);
+      const float pb = reduce_row<FMT, H>(acc[2 * p + 1], ro[2 * p + 1]);
+      const float score = finish_score(combine_halves(pa, pb), kscale);
+      const bool valid = full || (pos >= lo_l[p] && pos < hi_l[p]);
+      if constexpr (MODE == MODE_STORE) {
+        if (valid) E.out[row_l[p] * E.ld + (key - ks_l[p])] = score;
+      } else if constexpr (MODE == MODE_SAMPLE) {
+        if (valid) E.samp[row_l[p] * E.ns + pos] = score;
+      } else {
+        const bool pred = valid && score >= thr_l[p];
+        const uint64_t m = wave_ballot(pred);
+        if (m) {
+          const uint32_t mA = (uint32_t)m, mB = (uint32_t)(m >> 32);
+          int baseA = 0, baseB = 0;
+          if (l == 0 && mA) baseA = atomicAdd(&E.cnt[row0 + 2 * p], __builtin_popcount(mA));
+          if (l == 32 && mB) baseB = atomicAdd(&E.cnt[row0 + 2 * p + 1], __builtin_popcount(mB));
+          baseA = readlane(baseA, 0);
+          baseB = readlane(baseB, 32);
+          const int slot = (half ? baseB : baseA) + mask_prefix(m) - (half ? __builtin_popcount(mA) : 0);
+          if (pred && slot < E.cap) {
+            const int64_t o = row_l[p] * E.cap + slot;
+            E.slab_s[o] = score;
+            E.slab_i[o] = (int32_t)(key - ks_l[p]);
+          }
+        }
+      }
+    }
+  };
+
+  // Two key buffers, alternating, so the next tile's loads overlap this tile's math.
+  KeyOperand ka, kb;
+  load_tile(ka, t0);
+  int t = t0;
+  for (; t + 1 < t1; t += 2) {
+    load_tile(kb, t + 1);
+    compute(ka, t);
+    if (t + 2 < t1) load_tile(ka, t + 2);
+    compute(kb, t + 1);
+  }
+  if (t < t1) compute(ka, t);
+}
+
 // ----------------------------------------------------------------------------- K1b
 
 struct ThrArgs {
@@ -369,10 +572,10 @@ static ScoreArgs score_args(const DevProblem& P) {
   return A;
 }
 
-static TileWork tile_work(int rows, int heads, int64_t positions, int chunk) {
+static TileWork tile_work(const DevProblem& P, int64_t positions, int chunk) {
   TileWork W;
-  const int rb = rows_per_block(heads);
-  W.nrb = (rows + rb - 1) / rb;
+  const int rb = rows_per_block_for(P);
+  W.nrb = (P.rows + rb - 1) / rb;
   W.chunk = chunk;
   W.nchunk = (int)((positions + chunk - 1) / chunk);
   if (W.nchunk < 1) W.nchunk = 1;
@@ -391,17 +594,18 @@ static hipError_t dispatch_score(const DevProblem& P, const EpiArgs& E, const Ti
   const ScoreArgs A = score_args(P);
   const dim3 grid = tile_grid(W), block(kThreads);
   const bool paged = P.page_table != nullptr;
+  constexpr int RW = kRowsPerWave;
   if (P.fmt == FMT_E4M3) {
     if (P.heads == 64) {
       if (paged) score_kernel<FMT_E4M3, 64, MODE, true><<<grid, block, 0, s>>>(A, E, W);
-      else score_kernel<FMT_E4M3, 64, MODE, false><<<grid, block, 0, s>>>(A, E, W);
+      else score_tiles_kernel<FMT_E4M3, 64, MODE, RW><<<grid, block, 0, s>>>(A, E, W);
     } else {
       if (paged) score_kernel<FMT_E4M3, 32, MODE, true><<<grid, block, 0, s>>>(A, E, W);
-      else score_kernel<FMT_E4M3, 32, MODE, false><<<grid, block, 0, s>>>(A, E, W);
+      else score_tiles_kernel<FMT_E4M3, 32, MODE, RW><<<grid, block, 0, s>>>(A, E, W);
     }
   } else {
-    if (P.heads == 64) score_kernel<FMT_MXFP4, 64, MODE, false><<<grid, block, 0, s>>>(A, E, W);
-    else score_kernel<FMT_MXFP4, 32, MODE, false><<<grid, block, 0, s>>>(A, E, W);
+    if (P.heads == 64) score_tiles_kernel<FMT_MXFP4, 64, MODE, RW><<<grid, block, 0, s>>>(A, E, W);
+    else score_tiles_kernel<FMT_MXFP4, 32, MODE, RW><<<grid, block, 0, s>>>(A, E, W);
   }
   return hipGetLastError();
 }
@@ -414,7 +618,7 @@ hipError_t launch_score_store(const DevProblem& P, float* out, int64_t ld, hipSt
   EpiArgs E = {};
   E.out = out;
   E.ld = ld;
-  return dispatch_score<MODE_STORE>(P, E, tile_work(P.rows, P.heads, P.key_span, kChunkKeys), s);
+  return dispatch_score<MODE_STORE>(P, E, tile_work(P, P.key_span, kChunkKeys), s);
 }
 
 hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_idx, hipStream_t s, hipEvent_t* ev) {
@@ -430,7 +634,7 @@ hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_id
     E.stride = F.stride;
     E.skip_le = F.cap;
     if (F.debug_mode != 0 && F.debug_row_mod <= 0) E.skip_le = 0x7FFFFFFF;  // every row forced
-    if ((e = dispatch_score<MODE_SAMPLE>(P, E, tile_work(P.rows, P.heads, F.ns, kChunkSamples), s)) != hipSuccess)
+    if ((e = dispatch_score<MODE_SAMPLE>(P, E, tile_work(P, F.ns, kChunkSamples), s)) != hipSuccess)
       return e;
     if ((e = mark(1)) != hipSuccess) return e;
   }
@@ -449,7 +653,7 @@ hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_id
     T.cap = F.cap;
     T.ns = F.ns;
     T.stride = F.stride;
-    T.rb_rows = rows_per_block(P.heads);
+    T.rb_rows = rows_per_block_for(P);
     T.debug_mode = F.debug_mode;
     T.debug_row_mod = F.debug_row_mod;
     threshold_kernel<<<dim3(P.rows), dim3(kThreads), 0, s>>>(T);
@@ -464,7 +668,7 @@ hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_id
     E.slab_s = F.slab_s;
     E.slab_i = F.slab_i;
     E.cap = F.cap;
-    if ((e = dispatch_score<MODE_FILTER>(P, E, tile_work(P.rows, P.heads, P.key_span, kChunkKeys), s)) != hipSuccess)
+    if ((e = dispatch_score<MODE_FILTER>(P, E, tile_work(P, P.key_span, kChunkKeys), s)) != hipSuccess)
       return e;
     if ((e = mark(3)) != hipSuccess) return e;
   }

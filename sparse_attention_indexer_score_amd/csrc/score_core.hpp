@@ -149,6 +149,11 @@ __device__ __forceinline__ void load_key_lds(KeyOperand& ko, const uint8_t* row_
   }
 }
 
+// max(x, 0) for finite x as one integer max on the bit pattern: non-negative floats have
+// non-negative int32 patterns in the same order, negative floats (and -0.0) negative ones,
+// so the result is x or +0.0.  Unlike fmaxf it needs no NaN-quieting canonicalisation.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // Per-lane partial of sum_h w_h * max(dot_h, 0) over the heads this lane holds.
 template <int FMT, int H>
 __device__ __forceinline__ float row_partial(const RowOperand<FMT, H>& ro, const KeyOperand& ko) {
@@ -162,7 +167,7 @@ __device__ __forceinline__ float row_partial(const RowOperand<FMT, H>& ro, const
     acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ro.a[mt][1], ko.b[1], acc, C, C, 0, ro.sa[mt][1], 0,
                                                           ko.sb[1]);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) p = __builtin_fmaf(ro.w[mt][i], __builtin_fmaxf(acc[i], 0.0f), p);
+    for (int i = 0; i < 16; ++i) p = __builtin_fmaf(ro.w[mt][i], relu(acc[i]), p);
   }
   return p;
 }
