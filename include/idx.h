@@ -129,9 +129,15 @@ typedef struct idx_stats {
  * idx_score — materialised scores (the role of DeepGEMM mqa_logits, LiteTopK page,
  * introduction).  Writes out[r * ld + (s - ks[r])] (fp32) for every visible key s of
  * row r and nothing else.  ld >= max over rows of (ke - ks); out: fp32 [rows][ld].
+ *   ws   workspace of idx_score_workspace(p) bytes (may be NULL when that is 0); it holds
+ *        per-row constants the scoring kernels derive from q and w.
  * Scores are bitwise identical to those idx_fused_topk selects from (same scoring
  * core; LiteTopK page, section 1: only the epilogue differs).                        */
-int idx_score(const idx_problem* p, float* out, int64_t ld, void* stream);
+int idx_score(const idx_problem* p, float* out, int64_t ld, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace idx_score needs for this problem (host only; scalar fields only).
+ * Returns 0 when none is needed or the arguments are invalid.                       */
+size_t idx_score_workspace(const idx_problem* p);
 
 /* ------------------------------------------------------------------ selection
  * idx_select — exact top-k over materialised fp32 rows (ROCm DSA indexer top-k page:

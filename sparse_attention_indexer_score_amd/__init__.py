@@ -71,7 +71,8 @@ def _lib():
         i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         P = ctypes.POINTER(IdxProblem)
         sig = {
-            "idx_score": (ctypes.c_int, [P, _c_p, i64, _c_p]),
+            "idx_score": (ctypes.c_int, [P, _c_p, i64, _c_p, sz, _c_p]),
+            "idx_score_workspace": (sz, [P]),
             "idx_select": (ctypes.c_int, [_c_p, i64, _c_p, _c_p, i32, i32, _c_p, _c_p, sz, _c_p]),
             "idx_select_split": (ctypes.c_int, [_c_p, i64, _c_p, _c_p, i32, i32, _c_p, _c_p, sz, i32, _c_p]),
             "idx_row_split": (i32, [i32, i64, i32]),
@@ -182,6 +183,11 @@ class DeviceProblem:
 
 # ----------------------------------------------------------------------------- scoring
 
+def idx_score_workspace(prob: DeviceProblem) -> int:
+    s = prob.struct()
+    return int(_lib().idx_score_workspace(ctypes.byref(s)))
+
+
 def idx_score(prob: DeviceProblem, out: Optional[torch.Tensor] = None, ld: Optional[int] = None,
               stream=None) -> torch.Tensor:
     """Materialised fp32 scores: out[r, s - ks[r]] for every visible key (other entries untouched)."""
@@ -190,7 +196,10 @@ def idx_score(prob: DeviceProblem, out: Optional[torch.Tensor] = None, ld: Optio
     if out is None:
         out = torch.full((prob.rows, ld), float("nan"), dtype=torch.float32, device=prob.device)
     s = prob.struct()
-    _check(_lib().idx_score(ctypes.byref(s), _ptr(out), ld, _stream(stream)), "idx_score")
+    nb = int(_lib().idx_score_workspace(ctypes.byref(s)))
+    ws = _workspace(nb, prob.device)
+    _check(_lib().idx_score(ctypes.byref(s), _ptr(out), ld, _ptr(ws) if nb else None, nb, _stream(stream)),
+           "idx_score")
     return out
 
 

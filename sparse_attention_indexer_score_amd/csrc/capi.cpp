@@ -98,7 +98,7 @@ int check_problem(const idx_problem* p, DevProblem* out) {
 struct FusedSizes {
   int32_t cap, stride, ns, fb_blocks;
   int64_t key_span, scratch_ld;
-  size_t off_thr, off_cnt, off_stats, off_fb, off_slab_s, off_slab_i, off_samp, off_scratch, total;
+  size_t off_thr, off_cnt, off_stats, off_fb, off_slab_s, off_slab_i, off_samp, off_scratch, off_lin, total;
 };
 
 FusedSizes fused_sizes(const idx_problem* p, int32_t k) {
@@ -130,6 +130,8 @@ FusedSizes fused_sizes(const idx_problem* p, int32_t k) {
   o = round_up(o + rows * (size_t)z.ns * 4, kAlign);
   z.off_scratch = o;
   o = round_up(o + (size_t)z.fb_blocks * (size_t)z.scratch_ld * 4, kAlign);
+  z.off_lin = o;
+  o = round_up(o + (paged ? 0 : lin_ws_bytes((int32_t)rows)), kAlign);
   z.total = o;
   return z;
 }
@@ -224,7 +226,13 @@ int idx_select(const float* scores, int64_t ld, const int32_t* row_start, const 
   return idx_select_split(scores, ld, row_start, len, rows, k, out_idx, ws, ws_bytes, g, stream);
 }
 
-int idx_score(const idx_problem* p, float* out, int64_t ld, void* stream) {
+size_t idx_score_workspace(const idx_problem* p) {
+  if (check_problem(p, nullptr) != IDX_OK) return 0;
+  if (p->page_table || p->rows == 0) return 0;
+  return lin_ws_bytes(p->rows);
+}
+
+int idx_score(const idx_problem* p, float* out, int64_t ld, void* ws, size_t ws_bytes, void* stream) {
   DevProblem P;
   int rc = check_problem(p, &P);
   if (rc) return rc;
@@ -232,8 +240,11 @@ int idx_score(const idx_problem* p, float* out, int64_t ld, void* stream) {
   if (ld < 0) return IDX_EINVAL;
   if (!aligned(out, 4)) return IDX_EALIGN;
   if (p->rows == 0) return IDX_OK;
+  const size_t need = idx_score_workspace(p);
+  if (need > 0 && (!ws || ws_bytes < need)) return IDX_EWS;
+  if (need > 0 && !aligned(ws, kAlign)) return IDX_EALIGN;
   if ((rc = current_device(nullptr))) return rc;
-  return hip_err(launch_score_store(P, out, ld, static_cast<hipStream_t>(stream)));
+  return hip_err(launch_score_store(P, out, ld, ws, static_cast<hipStream_t>(stream)));
 }
 
 size_t idx_fused_workspace(const idx_problem* p, int32_t k) {
@@ -282,6 +293,8 @@ int idx_fused_topk(const idx_problem* p, int32_t k, int32_t* out_idx, void* ws, 
   F.slab_i = reinterpret_cast<int32_t*>(base + z.off_slab_i);
   F.samp = reinterpret_cast<float*>(base + z.off_samp);
   F.scratch = reinterpret_cast<float*>(base + z.off_scratch);
+  F.lin_q8 = F.lin_sf = nullptr;
+  if (!p->page_table) lin_carve(base + z.off_lin, p->rows, &F.lin_q8, &F.lin_sf);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((rc = hip_err(launch_fused(P, F, out_idx, s, next_timing_slot())))) return rc;
   if (stats) {

@@ -16,25 +16,23 @@
 //   K4   fallback_kernel          re-score a queued row into scratch and select exactly
 // If count >= min(k, V) and count <= cap, the slab holds every key whose score reaches the
 // k-th largest score, so selecting over it equals selecting over the whole row.
+#include <type_traits>
+
 #include "launch.hpp"
 #include "score_core.hpp"
 #include "select_core.hpp"
 
 namespace idx {
 
-enum : int { MODE_STORE = 0, MODE_FILTER = 1, MODE_SAMPLE = 2 };
+enum : int { MODE_STORE = 0, MODE_FILTER = 1, MODE_SAMPLE = 2, MODE_ROWSTORE = 3 };
 
 constexpr int kThreads = 256;  // 4 waves per workgroup
 constexpr int kTile = 32;      // keys per MFMA block
 
-#ifndef IDX_ROWS_PER_WAVE
-#define IDX_ROWS_PER_WAVE 2
-#endif
-constexpr int kRowsPerWave = IDX_ROWS_PER_WAVE;  // rows per wave of the contiguous-K kernel
-
-// Rows per workgroup of the paged kernel (score_kernel) and of score_tiles_kernel.
+// Rows per workgroup: 4 waves x 2 rows (contiguous kernel); the paged kernel holds 4 rows
+// per wave at 32 heads.
+int rows_per_block(int heads) { return 8; }
 static int rows_per_block_paged(int heads) { return 4 * (heads == 64 ? 2 : 4); }
-int rows_per_block(int heads) { return 4 * kRowsPerWave; }
 static int rows_per_block_for(const DevProblem& P) {
   return P.page_table ? rows_per_block_paged(P.heads) : rows_per_block(P.heads);
 }
@@ -81,6 +79,8 @@ struct EpiArgs {
   int32_t ns;
   int32_t stride;
   int32_t skip_le;  // SAMPLE: rows with ke - ks <= skip_le need no samples
+  // ROWSTORE
+  int32_t only_row;
 };
 
 struct TileWork {
@@ -223,39 +223,153 @@ __global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs A, EpiArgs E,
   }
 }
 
-// Contiguous-K scoring kernel (STORE / FILTER / SAMPLE epilogues).
+// ============================================================================= contiguous K
 //
-// Every row of a workgroup reads the same keys, so a wave holds RW rows' query operands in
-// registers and streams 32-key tiles: the tile's key operand is loaded once per wave
-// (scalar tile base + per-lane offset, next tile prefetched) and multiplied against all RW
-// rows.  Row ranges are wave-uniform and kept in scalar registers; a tile that lies inside
-// every row's range takes a branch-free path that issues all MFMAs before the head-reduce
-// VALU work, so the reduce of one row overlaps the MFMAs of the next.
+// Main scoring core for contiguous keys.  Per (row, key):
+//
+//   score = kscale * 0.5 * (L + A),   A = sum_h w_h |x_h|,   L = sum_h w_h x_h,
+//
+// which equals kscale * sum_h w_h max(x_h, 0) because max(x, 0) = (x + |x|) / 2.  A costs
+// one VALU fma (abs source modifier) per head in the head reduce.  L is linear in the key:
+// L = u . k with u = sum_h w_h q_h, so it runs on the matrix cores.  u is split into
+// kPieces fp6 (e2m3) vectors with e8m0 block scales: each piece takes the top 4
+// significant bits of its block's largest residual, so the residual shrinks at least 16x
+// per piece (below 2^-20 of the block maximum after five; exact for integer u).  One extra
+// pair of MFMAs per tile multiplies up to three row pairs' pieces against the same key
+// operand; fp6 runs at the fp4 MFMA rate.  Every kernel that produces a
+// score for contiguous keys (materialised scores, samples, fused filter, fallback) runs
+// wg_tiles() below, so a (row, key) always gets the same instruction sequence, the same
+// MFMA row/column and the same summation order: the scores are bitwise identical.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-template <int FMT>
-__device__ __forceinline__ void load_key_at(KeyOperand& ko, const uint8_t* kbase, const uint8_t* sfbase,
-                                            uint32_t off, uint32_t sf_off) {
-  constexpr int KB = Fmt<FMT>::kBytes;
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    if constexpr (FMT == FMT_E4M3) {
-      const v4i x0 = *reinterpret_cast<const v4i*>(kbase + off + ks * (KB / 2));
-      const v4i x1 = *reinterpret_cast<const v4i*>(kbase + off + ks * (KB / 2) + 16);
-      ko.b[ks] = v8i{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-      ko.sb[ks] = 127;
-    } else {
-      const v4i x = *reinterpret_cast<const v4i*>(kbase + off + ks * (KB / 2));
-      ko.b[ks] = v8i{x.x, x.y, x.z, x.w, 0, 0, 0, 0};
-    }
+constexpr int kPieces = 5;
+constexpr int kLinRowBytes = kPieces * 2 * 2 * 32;  // pieces x ksteps x halves x 32 bytes (24 used)
+constexpr int kLinRowScales = kPieces * 2 * 2;
+
+// Rows per wave of the contiguous kernel (register budget of the pipelined tile loop).
+template <int H>
+struct RowsPerWave {
+  static constexpr int value = 2;
+};
+
+struct LinArgs {
+  const uint8_t* q8;  // [rows][kPieces][2 ksteps][2 halves][32]: fp6 pieces of u, MFMA lane order
+  const uint8_t* sf;  // [rows][kPieces][2][2]: e8m0 scale of hardware block (kstep, half)
+};
+
+// ---- preparation: u = sum_h w_h q_h and its pieces, one workgroup of 128 threads per row.
+//
+// gfx950 operand layouts of v_mfma_scale_f32_32x32x64_f8f6f4 (measured): fp4 and fp6 lanes
+// hold K elements [32h, 32h + 32) of lane half h, element p at bits [bits*p, bits*(p+1));
+// fp8 byte j of lane half h is K element 16h + j (j < 16) or 32 + 16h + (j - 16); the
+// scale of lane half b covers K block [32b, 32b + 32).  MXFP4 keys are in hardware K
+// order; e4m3 keys are loaded with byte j of half h = head_dim element 32h + j, i.e. K
+// element k holds head_dim element kelem(k).  Piece element p of half h sits at K = 32h + p
+// and must hold the head_dim element the key has there.
+__device__ __forceinline__ int lin_elem(bool key_fp4, int h, int p) {
+  const int k = 32 * h + p;
+  if (key_fp4) return k;
+  return k < 32 ? 32 * (k / 16) + k % 16 : 32 * ((k - 32) / 16) + 16 + (k - 32) % 16;
+}
+
+__device__ __forceinline__ float e2m1_value(int code) {
+  const int e = (code >> 1) & 3, m = code & 1;
+  const float v = e == 0 ? 0.5f * (float)m : ldexpf((float)(2 + m), e - 2);
+  return (code & 8) ? -v : v;
+}
+
+__device__ __forceinline__ float e4m3_value(int b) {
+  const int e = (b >> 3) & 15, m = b & 7;
+  const float v = e == 0 ? ldexpf((float)m, -9) : ldexpf((float)(8 + m), e - 10);
+  return (b & 0x80) ? -v : v;
+}
+
+// fp6 e2m3 (sign, 2-bit exponent with bias 1, 3-bit mantissa; subnormal step 1/8).
+__device__ __forceinline__ float e2m3_value(int c) {
+  const int e = (c >> 3) & 3, m = c & 7;
+  const float v = e == 0 ? 0.125f * (float)m : ldexpf((float)(8 + m), e - 4);
+  return (c & 0x20) ? -v : v;
+}
+
+// Round y (|y| < 4) to e2m3, nearest with ties to even; returns the 6-bit code.
+__device__ __forceinline__ int e2m3_encode(float y) {
+  const int sign = y < 0.0f ? 0x20 : 0;
+  const float a = fabsf(y);
+  if (a < 1.0f) {
+    const int m = (int)__builtin_rintf(a * 8.0f);
+    return sign | (m == 8 ? 0x08 : m);
   }
-  if constexpr (FMT == FMT_MXFP4) {
-    const int half = lane_id() >> 5;
-    const uint32_t sw = *reinterpret_cast<const uint32_t*>(sfbase + sf_off);
-    ko.sb[0] = (sw >> (8 * half)) & 0xFF;
-    ko.sb[1] = (sw >> (8 * (2 + half))) & 0xFF;
+  if (a < 2.0f) {
+    const int m = (int)__builtin_rintf((a - 1.0f) * 8.0f);
+    return sign | (m == 8 ? 0x10 : 0x08 | m);
+  }
+  const int m = (int)__builtin_rintf((0.5f * a - 1.0f) * 8.0f);
+  return sign | (m == 8 ? 0x18 : 0x10 | m);
+}
+
+template <int FMT, int H>
+__global__ __launch_bounds__(128) void lin_prep_kernel(const uint8_t* q, const uint8_t* q_sf, const uint16_t* w,
+                                                       int rows, bool key_fp4, uint8_t* lin_q8, uint8_t* lin_sf) {
+  __shared__ float res[128];
+  __shared__ float bmax[4];
+  __shared__ uint32_t packed[kPieces][2][2][6];
+  const int r = blockIdx.x;
+  const int d = threadIdx.x;  // head_dim element
+  float u = 0.0f;
+  for (int h = 0; h < H; ++h) {
+    const int64_t hv = (int64_t)r * H + h;
+    float qd;
+    if constexpr (FMT == FMT_E4M3) {
+      qd = e4m3_value(q[hv * 128 + d]);
+    } else {
+      const int byte = q[hv * 64 + d / 2];
+      qd = ldexpf(e2m1_value((d & 1) ? byte >> 4 : byte & 15), (int)q_sf[hv * 4 + d / 32] - 127);
+    }
+    u = __builtin_fmaf(bf16_to_f32(w[hv]), qd, u);
+  }
+  // Where element d sits in the pieces: kstep, lane half (= scale block) and position.
+  const int ks = d / 64, e = d % 64;
+  int hh = 0, pp = 0;
+  for (int h = 0; h < 2; ++h)
+    for (int p = 0; p < 32; ++p)
+      if (lin_elem(key_fp4, h, p) == e) {
+        hh = h;
+        pp = p;
+      }
+  if (d < kPieces * 2 * 2 * 6) (&packed[0][0][0][0])[d] = 0;
+  float rd = u;
+  for (int c = 0; c < kPieces; ++c) {
+    res[ks * 64 + hh * 32 + pp] = fabsf(rd);
+    __syncthreads();
+    if (d < 4) {
+      float m = 0.0f;
+      for (int p = 0; p < 32; ++p) m = fmaxf(m, res[d * 32 + p]);
+      bmax[d] = m;
+    }
+    __syncthreads();
+    const float m = bmax[ks * 2 + hh];
+    int sexp = -127;  // block scale 2^sexp: the block maximum maps into [2, 4)
+    if (m > 0.0f) {
+      int ex;
+      frexpf(m, &ex);
+      sexp = max(-127, min(127, ex - 2));
+    }
+    const int code = e2m3_encode(ldexpf(rd, -sexp));
+    rd -= ldexpf(e2m3_value(code), sexp);
+    const int bit = 6 * pp;
+    atomicOr(&packed[c][ks][hh][bit / 32], (uint32_t)code << (bit % 32));
+    if (bit % 32 > 26) atomicOr(&packed[c][ks][hh][bit / 32 + 1], (uint32_t)code >> (32 - bit % 32));
+    if (pp == 0) lin_sf[(((int64_t)r * kPieces + c) * 2 + ks) * 2 + hh] = (uint8_t)(sexp + 127);
+    __syncthreads();
+  }
+  for (int i = d; i < kPieces * 2 * 2 * 8; i += 128) {
+    const int c = i / 32, k2 = (i / 16) % 2, h2 = (i / 8) % 2, wd = i % 8;
+    const uint32_t v = wd < 6 ? packed[c][k2][h2][wd] : 0u;
+    reinterpret_cast<uint32_t*>(lin_q8)[((((int64_t)r * kPieces + c) * 2 + k2) * 2 + h2) * 8 + wd] = v;
   }
 }
+
+// ---- the wave-level tile routine
 
 template <int FMT, int H>
 __device__ __forceinline__ void mfma_row(v16f (&acc)[H / 32], const RowOperand<FMT, H>& ro, const KeyOperand& ko) {
@@ -269,35 +383,112 @@ __device__ __forceinline__ void mfma_row(v16f (&acc)[H / 32], const RowOperand<F
   }
 }
 
-// Same arithmetic, in the same order, as row_partial().
+// Per-lane partial of sum_h w_h |x_h| over the heads this lane holds.
 template <int FMT, int H>
-__device__ __forceinline__ float reduce_row(const v16f (&acc)[H / 32], const RowOperand<FMT, H>& ro) {
+__device__ __forceinline__ float reduce_abs(const v16f (&acc)[H / 32], const RowOperand<FMT, H>& ro) {
   float p = 0.0f;
 #pragma unroll
   for (int mt = 0; mt < H / 32; ++mt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) p = __builtin_fmaf(ro.w[mt][i], relu(acc[mt][i]), p);
+    for (int i = 0; i < 16; ++i) p = __builtin_fmaf(ro.w[mt][i], __builtin_fabsf(acc[mt][i]), p);
   return p;
 }
 
-template <int FMT, int H, int MODE, int RW>
-__global__ __launch_bounds__(kThreads) void score_tiles_kernel(ScoreArgs A, EpiArgs E, TileWork W) {
+// Pieces of up to three row pairs of a wave as the A operand of the linear MFMA: lane l
+// supplies M row (l % 32) = 8g + 4hh + j, slot s = 4g + j holds piece (s % 5) of row
+// row0 + 2 (s / 5) + hh.  In the result, lane half H then holds in accumulator s the
+// piece dot products of row row0 + 2 (s / 5) + H, the row its head sums land on.
+struct LinOperand {
+  v8i a[2];
+  int sa[2];
+};
+
+__device__ __forceinline__ void load_lin(LinOperand& lo, const LinArgs& L, int row0, int rows, int npairs) {
+  const int l = lane_id();
+  const int m = l & 31, half = l >> 5;
+  const int s = 4 * (m >> 3) + (m & 3), hh = (m >> 2) & 1;
+  const int p = s / kPieces, c = s % kPieces;
+  const int row = row0 + 2 * p + hh;
+  const bool ok = p < npairs && row < rows;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    if (ok) {
+      const int64_t base = (((int64_t)row * kPieces + c) * 2 + ks) * 2 + half;
+      const v4i x0 = *reinterpret_cast<const v4i*>(L.q8 + base * 32);
+      const int2 x1 = *reinterpret_cast<const int2*>(L.q8 + base * 32 + 16);
+      lo.a[ks] = v8i{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, 0, 0};
+      lo.sa[ks] = L.sf[base];
+    } else {
+      lo.a[ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      lo.sa[ks] = 127;
+    }
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ v16f mfma_lin(const LinOperand& lo, const KeyOperand& ko) {
+  constexpr int C = Fmt<FMT>::kCode;
+  v16f a = {};
+  a = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(lo.a[0], ko.b[0], a, 2, C, 0, lo.sa[0], 0, ko.sb[0]);
+  a = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(lo.a[1], ko.b[1], a, 2, C, 0, lo.sa[1], 0, ko.sb[1]);
+  return a;
+}
+
+__device__ __forceinline__ float lin_of_pair(const v16f& a, int p) {
+  const int s = kPieces * p;
+  float x = a[s];
+#pragma unroll
+  for (int c = 1; c < kPieces; ++c) x = x + a[s + c];
+  return x;
+}
+
+__device__ __forceinline__ float finish_score2(float abs_sum, float lin, float kscale) {
+  return ((lin + abs_sum) * 0.5f) * kscale;
+}
+
+// Key tiles are staged through LDS: all four waves of a workgroup use the same keys, so a
+// stage of kStageTiles 32-key tiles is fetched once per workgroup with coalesced 16-byte
+// loads (issued one stage ahead, double-buffered, one barrier per stage) and each wave
+// reads its MFMA key operands from LDS.  Rows are padded to KB + 16 bytes so that the 8
+// lanes of a 16-byte LDS read phase hit distinct banks.
+constexpr int kStageTiles = 4;
+
+template <int FMT>
+struct StageGeom {
+  static constexpr int kKB = Fmt<FMT>::kBytes;
+  static constexpr int kStride = kKB + 16;
+  static constexpr int kKeys = kStageTiles * kTile;        // 128 keys per stage
+  static constexpr int kBytes = kKeys * kStride;           // codes of one stage
+  static constexpr int kChunks = kKeys * kKB / 16;          // 16-byte loads per stage
+  static constexpr int kPerThread = kChunks / kThreads;     // fp4: 2, fp8: 4
+  static_assert(kChunks % kThreads == 0, "stage must split evenly");
+};
+
+template <int FMT>
+struct StageLds {
+  uint8_t* codes;  // [2][kKeys * kStride]
+  uint32_t* sf;    // [2][kKeys] e8m0 words (MXFP4)
+  float* ks;       // [2][kKeys] per-key scale (1.0 when absent)
+};
+
+// Scores of the RW rows [row0, row0 + RW) of this wave on the workgroup's tiles [tA, tB)
+// (positions: keys, or sample slots with key = phase + pos * S), with the epilogue of MODE.
+// Every wave of the workgroup must call it with the same tA, tB.  MAIN mode: every wave
+// scores every tile that meets its rows.  FALLBACK mode: all waves hold the same rows and
+// wave w scores tile w of each stage; MODE_ROWSTORE then writes only row E.only_row, to
+// E.out[key - ks].
+template <int FMT, int H, int MODE, int RW, bool FALLBACK>
+__device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, const EpiArgs& E, int row0,
+                                         int phase, int S, int c0, int c1, int tA, int tB,
+                                         const StageLds<FMT>& sl) {
   static_assert(RW % 2 == 0, "rows are processed in pairs");
-  constexpr int KB = Fmt<FMT>::kBytes;
-  constexpr int RB = 4 * RW;
+  using G = StageGeom<FMT>;
+  constexpr int KB = G::kKB;
   constexpr int NP = RW / 2;
-  const int64_t item = map_item(W);
-  if (item >= W.total) return;
-  const int rb = (int)(item % W.nrb);
-  const int chunk = (int)(item / W.nrb);
-  const int wave = uniform(threadIdx.x / kWave);
   const int l = lane_id();
   const int half = l >> 5, col = l & 31;
-  const int row0 = rb * RB + wave * RW;
-  const int S = (MODE == MODE_SAMPLE) ? E.stride : 1;
-  const int phase = (MODE == MODE_SAMPLE) ? sample_phase(rb, S) : 0;
+  const int wave = uniform(threadIdx.x / kWave);
 
-  // Row ranges in position space (keys, or sample slots), wave-uniform.
   int plo[RW], phi[RW], ksr[RW];
   int wlo = 0x7FFFFFFF, whi = 0, full_lo = 0, full_hi = 0x7FFFFFFF;
 #pragma unroll
@@ -321,16 +512,15 @@ __global__ __launch_bounds__(kThreads) void score_tiles_kernel(ScoreArgs A, EpiA
     full_lo = max(full_lo, plo[i]);
     full_hi = min(full_hi, phi[i]);
   }
-  const int c0 = chunk * W.chunk, c1 = c0 + W.chunk;
-  const int t0 = max(c0, wlo) / kTile, t1 = (min(c1, whi) + kTile - 1) / kTile;
-  if (t0 >= t1) return;
+  const int wt0 = max(c0, wlo) / kTile, wt1 = (min(c1, whi) + kTile - 1) / kTile;  // this wave's tiles
 
   RowOperand<FMT, H> ro[RW];
 #pragma unroll
   for (int i = 0; i < RW; ++i)
     if (row0 + i < A.rows) load_row<FMT, H>(ro[i], A, row0 + i);
+  LinOperand lo;
+  load_lin(lo, L, row0, A.rows, NP);
 
-  // Per-lane constants of each row pair: lanes 0-31 carry row 2p, lanes 32-63 row 2p+1.
   float thr_l[NP];
   int ks_l[NP], lo_l[NP], hi_l[NP];
   int64_t row_l[NP];
@@ -344,42 +534,25 @@ __global__ __launch_bounds__(kThreads) void score_tiles_kernel(ScoreArgs A, EpiA
     thr_l[p] = 0.0f;
     if (MODE == MODE_FILTER && row0 + i < A.rows) thr_l[p] = E.thr[row0 + i];
   }
-
-  const int64_t kstep = (int64_t)kTile * S;                 // keys per tile
-  const uint32_t off = (uint32_t)(col * S) * KB + half * (KB / 4);
-  const uint32_t sf_off = (uint32_t)(col * S) * 4;
   const int64_t last_key = A.num_keys - 1;
-  auto tile_key0 = [&](int t) -> int64_t { return (int64_t)phase + (int64_t)t * kstep; };
-  auto load_tile = [&](KeyOperand& ko, int t) {
-    const int64_t k0 = tile_key0(t);
-    if (k0 + (kTile - 1) * (int64_t)S <= last_key) {
-      load_key_at<FMT>(ko, A.k + k0 * KB, A.k_sf + k0 * 4, off, sf_off);
-    } else {  // ragged tail: clamp every lane to a real key (results are masked)
-      int64_t key = k0 + (int64_t)col * S;
-      key = key < last_key ? key : last_key;
-      load_key_at<FMT>(ko, A.k + key * KB, A.k_sf + key * 4, half * (KB / 4), 0);
-    }
+  auto key_of = [&](int64_t pos) -> int64_t {
+    const int64_t key = (int64_t)phase + pos * S;
+    return key < last_key ? key : last_key;
   };
 
-  // One tile: MFMAs for all RW rows first, then the head reduce and epilogue per row pair.
-  // Rows that do not see (part of) the tile are computed anyway and masked per lane.
-  auto compute = [&](const KeyOperand& kc, int t) {
+  // Epilogue of one tile for every row pair, given the pairs' packed scores.
+  auto epilogue = [&](int t, const float* score_of) {
     const int pos = t * kTile + col;
-    const int64_t key = tile_key0(t) + (int64_t)col * S;
+    const int64_t key = (int64_t)phase + (int64_t)pos * S;
     const bool full = t * kTile >= full_lo && (t + 1) * kTile <= full_hi;  // wave-uniform
-    float kscale = 1.0f;
-    if (A.k_scale) kscale = A.k_scale[key < last_key ? key : last_key];
-    v16f acc[RW][H / 32];
-#pragma unroll
-    for (int i = 0; i < RW; ++i) mfma_row<FMT, H>(acc[i], ro[i], kc);
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      const float pa = reduce_row<FMT, H>(acc[2 * p], ro[2 * p]);
-      const float pb = reduce_row<FMT, H>(acc[2 * p + 1], ro[2 * p + 1]);
-      const float score = finish_score(combine_halves(pa, pb), kscale);
+      const float score = score_of[p];
       const bool valid = full || (pos >= lo_l[p] && pos < hi_l[p]);
       if constexpr (MODE == MODE_STORE) {
         if (valid) E.out[row_l[p] * E.ld + (key - ks_l[p])] = score;
+      } else if constexpr (MODE == MODE_ROWSTORE) {
+        if (valid && row_l[p] == E.only_row) E.out[key - ks_l[p]] = score;
       } else if constexpr (MODE == MODE_SAMPLE) {
         if (valid) E.samp[row_l[p] * E.ns + pos] = score;
       } else {
@@ -403,17 +576,148 @@ __global__ __launch_bounds__(kThreads) void score_tiles_kernel(ScoreArgs A, EpiA
     }
   };
 
-  // Two key buffers, alternating, so the next tile's loads overlap this tile's math.
-  KeyOperand ka, kb;
-  load_tile(ka, t0);
-  int t = t0;
-  for (; t + 1 < t1; t += 2) {
-    load_tile(kb, t + 1);
-    compute(ka, t);
-    if (t + 2 < t1) load_tile(ka, t + 2);
-    compute(kb, t + 1);
+  // Key operand and key scale of tile slot i of LDS stage buffer `buf`.
+  auto read_b = [&](int buf, int i, KeyOperand& ko, float& kscale) {
+    const int kidx = i * kTile + col;
+    const uint8_t* row = sl.codes + buf * G::kBytes + kidx * G::kStride;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if constexpr (FMT == FMT_E4M3) {
+        const v4i x0 = *reinterpret_cast<const v4i*>(row + ks * 64 + half * 32);
+        const v4i x1 = *reinterpret_cast<const v4i*>(row + ks * 64 + half * 32 + 16);
+        ko.b[ks] = v8i{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        ko.sb[ks] = 127;
+      } else {
+        const v4i x = *reinterpret_cast<const v4i*>(row + ks * 32 + half * 16);
+        ko.b[ks] = v8i{x.x, x.y, x.z, x.w, 0, 0, 0, 0};
+      }
+    }
+    if constexpr (FMT == FMT_MXFP4) {
+      const uint32_t sw = sl.sf[buf * G::kKeys + kidx];
+      ko.sb[0] = (sw >> (8 * half)) & 0xFF;
+      ko.sb[1] = (sw >> (8 * (2 + half))) & 0xFF;
+    }
+    kscale = sl.ks[buf * G::kKeys + kidx];
+  };
+  struct Acc {
+    v16f row[RW][H / 32];
+    v16f lin;
+  };
+  auto issue = [&](Acc& a, const KeyOperand& ko) {
+    a.lin = mfma_lin<FMT>(lo, ko);
+#pragma unroll
+    for (int r = 0; r < RW; ++r) mfma_row<FMT, H>(a.row[r], ro[r], ko);
+  };
+  auto reduce = [&](const Acc& a, float kscale, float* sc) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const float pa = reduce_abs<FMT, H>(a.row[2 * p], ro[2 * p]);
+      const float pb = reduce_abs<FMT, H>(a.row[2 * p + 1], ro[2 * p + 1]);
+      sc[p] = finish_score2(combine_halves(pa, pb), lin_of_pair(a.lin, p), kscale);
+    }
+  };
+  // One tile: key operand from LDS, MFMAs for all RW rows and the linear tile, reduce, epilogue.
+  auto compute = [&](int buf, int i, int t) {
+    KeyOperand ko;
+    float ksc;
+    read_b(buf, i, ko, ksc);
+    Acc a;
+    issue(a, ko);
+    float sc[NP];
+    reduce(a, ksc, sc);
+    epilogue(t, sc);
+  };
+
+  // Stage loads: thread c of the workgroup fetches 16-byte pieces c, c + 256, ... of the
+  // stage's key codes, and the block-scale word and key scale of key c (c < 128).
+  v4i regs[G::kPerThread];
+  uint32_t sfw = 0;
+  float ksv = 1.0f;
+  auto gload = [&](int stage) {
+    const int64_t pos0 = (int64_t)(tA + stage * kStageTiles) * kTile;
+#pragma unroll
+    for (int u = 0; u < G::kPerThread; ++u) {
+      const int c = threadIdx.x + u * kThreads;
+      const int key = c / (KB / 16), part = c % (KB / 16);
+      regs[u] = *reinterpret_cast<const v4i*>(A.k + key_of(pos0 + key) * KB + part * 16);
+    }
+    if (threadIdx.x < G::kKeys) {
+      const int64_t g = key_of(pos0 + threadIdx.x);
+      if constexpr (FMT == FMT_MXFP4) sfw = *reinterpret_cast<const uint32_t*>(A.k_sf + g * 4);
+      ksv = A.k_scale ? A.k_scale[g] : 1.0f;
+    }
+  };
+  auto lwrite = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < G::kPerThread; ++u) {
+      const int c = threadIdx.x + u * kThreads;
+      const int key = c / (KB / 16), part = c % (KB / 16);
+      *reinterpret_cast<v4i*>(sl.codes + buf * G::kBytes + key * G::kStride + part * 16) = regs[u];
+    }
+    if (threadIdx.x < G::kKeys) {
+      sl.sf[buf * G::kKeys + threadIdx.x] = sfw;
+      sl.ks[buf * G::kKeys + threadIdx.x] = ksv;
+    }
+  };
+
+  const int nst = (tB - tA + kStageTiles - 1) / kStageTiles;
+  gload(0);
+  lwrite(0);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    const bool more = st + 1 < nst;
+    if (more) gload(st + 1);
+    const int tbase = tA + st * kStageTiles;
+#pragma unroll
+    for (int i = 0; i < kStageTiles; ++i) {
+      const int t = tbase + i;
+      if (t >= tB) break;  // workgroup-uniform
+      const bool mine = FALLBACK ? (i == wave) : (t >= wt0 && t < wt1);
+      if (mine) compute(buf, i, t);
+    }
+    if (more) lwrite(buf ^ 1);
+    __syncthreads();
   }
-  if (t < t1) compute(ka, t);
+}
+
+template <int FMT>
+struct StageShared {
+  __attribute__((aligned(16))) uint8_t codes[2 * StageGeom<FMT>::kBytes];
+  uint32_t sf[2 * StageGeom<FMT>::kKeys];
+  float ks[2 * StageGeom<FMT>::kKeys];
+};
+
+template <int FMT, int H, int MODE>
+__global__ __launch_bounds__(kThreads) void score_tiles_kernel(ScoreArgs A, LinArgs L, EpiArgs E, TileWork W) {
+  constexpr int RW = RowsPerWave<H>::value;
+  __shared__ StageShared<FMT> sh;
+  const int64_t item = map_item(W);
+  if (item >= W.total) return;
+  const int rb = (int)(item % W.nrb);
+  const int chunk = (int)(item / W.nrb);
+  const int wave = uniform(threadIdx.x / kWave);
+  const int S = (MODE == MODE_SAMPLE) ? E.stride : 1;
+  const int phase = (MODE == MODE_SAMPLE) ? sample_phase(rb, S) : 0;
+  const int c0 = chunk * W.chunk, c1 = c0 + W.chunk;
+  // Tiles of the workgroup: the union of all its rows' ranges within the chunk.
+  int lo = 0x7FFFFFFF, hi = 0;
+  for (int r = rb * 4 * RW; r < min(A.rows, (rb + 1) * 4 * RW); ++r) {
+    const int ks = uniform(A.ks[r]), ke = uniform(A.ke[r]);
+    int plo = ks, phi = ke;
+    if (MODE == MODE_SAMPLE) {
+      plo = phi = 0;
+      if (ke - ks > E.skip_le) sample_range(ks, ke, phase, S, plo, phi);
+    }
+    if (phi > plo) {
+      lo = min(lo, plo);
+      hi = max(hi, phi);
+    }
+  }
+  const int tA = max(c0, lo) / kTile, tB = (min(c1, hi) + kTile - 1) / kTile;
+  if (tA >= tB) return;  // workgroup-uniform
+  const StageLds<FMT> sl{sh.codes, sh.sf, sh.ks};
+  wg_tiles<FMT, H, MODE, RW, false>(A, L, E, rb * 4 * RW + wave * RW, phase, S, c0, c1, tA, tB, sl);
 }
 
 // ----------------------------------------------------------------------------- K1b
@@ -513,8 +817,9 @@ struct FbArgs {
   int32_t k;
 };
 
+// Paged keys: the row is re-scored with score_kernel's core (row_partial).
 template <int FMT, int H>
-__global__ __launch_bounds__(kThreads) void fallback_kernel(ScoreArgs A, FbArgs F) {
+__global__ __launch_bounds__(kThreads) void fallback_paged_kernel(ScoreArgs A, FbArgs F) {
   __shared__ SelSmem sm;
   __shared__ int sh_item;
   const int wave = threadIdx.x / kWave;
@@ -542,6 +847,43 @@ __global__ __launch_bounds__(kThreads) void fallback_kernel(ScoreArgs A, FbArgs 
       const float hs = combine_halves(p, p);
       const float score = finish_score(hs, key_scale(A, phys));
       if (l < 32 && valid) mine[pos - ks] = score;
+    }
+    __syncthreads();
+    const int need = min(F.k, V);
+    int32_t* out = F.out + (int64_t)r * F.k;
+    if (need > 0) block_select<kThreads>(RowSrc{mine}, V, need, out, sm);
+    for (int j = need + threadIdx.x; j < F.k; j += kThreads) out[j] = -1;
+    __syncthreads();
+  }
+}
+
+
+// Contiguous keys: the row is re-scored by wg_tiles() for the same pair of rows, tiles and
+// lane positions as in score_tiles_kernel (each wave takes one tile of every stage), so its
+// scores are bitwise the ones the slab was filtered with; only the row itself is stored.
+template <int FMT, int H>
+__global__ __launch_bounds__(kThreads) void fallback_tiles_kernel(ScoreArgs A, LinArgs L, FbArgs F) {
+  constexpr int RW = RowsPerWave<H>::value;
+  __shared__ SelSmem sm;
+  __shared__ StageShared<FMT> sh;
+  __shared__ int sh_item;
+  float* mine = F.scratch + (int64_t)blockIdx.x * F.scratch_ld;
+  const StageLds<FMT> sl{sh.codes, sh.sf, sh.ks};
+  for (;;) {
+    if (threadIdx.x == 0) sh_item = atomicAdd(&F.fb_ctrl[1], 1);
+    __syncthreads();
+    const int item = sh_item;
+    __syncthreads();
+    if (item >= F.fb_ctrl[0]) break;  // every wave sees the same item and count
+    const int r = F.fb_list[item];
+    const int ks = A.ks[r], ke = A.ke[r];
+    const int V = ke - ks;
+    if (V > 0) {
+      EpiArgs E = {};
+      E.out = mine;
+      E.only_row = r;
+      wg_tiles<FMT, H, MODE_ROWSTORE, RW, true>(A, L, E, (r / RW) * RW, 0, 1, ks, ke, ks / kTile,
+                                                (ke + kTile - 1) / kTile, sl);
     }
     __syncthreads();
     const int need = min(F.k, V);
@@ -589,23 +931,36 @@ static dim3 tile_grid(const TileWork& W) {
   return dim3((unsigned)(groups * 8 * W.nrb));
 }
 
+static LinArgs lin_args(const FusedPlan& F) { return LinArgs{F.lin_q8, F.lin_sf}; }
+
+// u = sum_h w_h q_h and its pieces for every row (contiguous keys only).
+static hipError_t launch_lin_prep(const DevProblem& P, uint8_t* q8, uint8_t* sf, hipStream_t s) {
+  const dim3 grid(P.rows), block(128);
+  const bool key_fp4 = P.fmt == FMT_MXFP4;
+  if (P.fmt == FMT_E4M3) {
+    if (P.heads == 64) lin_prep_kernel<FMT_E4M3, 64><<<grid, block, 0, s>>>(P.q, P.q_sf, P.w, P.rows, key_fp4, q8, sf);
+    else lin_prep_kernel<FMT_E4M3, 32><<<grid, block, 0, s>>>(P.q, P.q_sf, P.w, P.rows, key_fp4, q8, sf);
+  } else {
+    if (P.heads == 64) lin_prep_kernel<FMT_MXFP4, 64><<<grid, block, 0, s>>>(P.q, P.q_sf, P.w, P.rows, key_fp4, q8, sf);
+    else lin_prep_kernel<FMT_MXFP4, 32><<<grid, block, 0, s>>>(P.q, P.q_sf, P.w, P.rows, key_fp4, q8, sf);
+  }
+  return hipGetLastError();
+}
+
 template <int MODE>
-static hipError_t dispatch_score(const DevProblem& P, const EpiArgs& E, const TileWork& W, hipStream_t s) {
+static hipError_t dispatch_score(const DevProblem& P, const LinArgs& L, const EpiArgs& E, const TileWork& W,
+                                 hipStream_t s) {
   const ScoreArgs A = score_args(P);
   const dim3 grid = tile_grid(W), block(kThreads);
-  const bool paged = P.page_table != nullptr;
-  constexpr int RW = kRowsPerWave;
-  if (P.fmt == FMT_E4M3) {
-    if (P.heads == 64) {
-      if (paged) score_kernel<FMT_E4M3, 64, MODE, true><<<grid, block, 0, s>>>(A, E, W);
-      else score_tiles_kernel<FMT_E4M3, 64, MODE, RW><<<grid, block, 0, s>>>(A, E, W);
-    } else {
-      if (paged) score_kernel<FMT_E4M3, 32, MODE, true><<<grid, block, 0, s>>>(A, E, W);
-      else score_tiles_kernel<FMT_E4M3, 32, MODE, RW><<<grid, block, 0, s>>>(A, E, W);
-    }
+  if (P.page_table) {  // paged keys are e4m3 (checked at the boundary)
+    if (P.heads == 64) score_kernel<FMT_E4M3, 64, MODE, true><<<grid, block, 0, s>>>(A, E, W);
+    else score_kernel<FMT_E4M3, 32, MODE, true><<<grid, block, 0, s>>>(A, E, W);
+  } else if (P.fmt == FMT_E4M3) {
+    if (P.heads == 64) score_tiles_kernel<FMT_E4M3, 64, MODE><<<grid, block, 0, s>>>(A, L, E, W);
+    else score_tiles_kernel<FMT_E4M3, 32, MODE><<<grid, block, 0, s>>>(A, L, E, W);
   } else {
-    if (P.heads == 64) score_tiles_kernel<FMT_MXFP4, 64, MODE, RW><<<grid, block, 0, s>>>(A, E, W);
-    else score_tiles_kernel<FMT_MXFP4, 32, MODE, RW><<<grid, block, 0, s>>>(A, E, W);
+    if (P.heads == 64) score_tiles_kernel<FMT_MXFP4, 64, MODE><<<grid, block, 0, s>>>(A, L, E, W);
+    else score_tiles_kernel<FMT_MXFP4, 32, MODE><<<grid, block, 0, s>>>(A, L, E, W);
   }
   return hipGetLastError();
 }
@@ -613,12 +968,30 @@ static hipError_t dispatch_score(const DevProblem& P, const EpiArgs& E, const Ti
 constexpr int kChunkKeys = 4096;
 constexpr int kChunkSamples = 1024;
 
-hipError_t launch_score_store(const DevProblem& P, float* out, int64_t ld, hipStream_t s) {
+size_t lin_ws_bytes(int32_t rows) {
+  return (size_t)rows * kLinRowBytes + (((size_t)rows * kLinRowScales + 255) & ~(size_t)255) + 256;
+}
+
+void lin_carve(void* ws, int32_t rows, uint8_t** q8, uint8_t** sf) {
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  *q8 = p;
+  *sf = p + (size_t)rows * kLinRowBytes;
+}
+
+hipError_t launch_score_store(const DevProblem& P, float* out, int64_t ld, void* ws, hipStream_t s) {
   if (P.rows == 0) return hipSuccess;
+  LinArgs L = {nullptr, nullptr};
+  if (!P.page_table) {
+    uint8_t *q8, *sf;
+    lin_carve(ws, P.rows, &q8, &sf);
+    hipError_t e = launch_lin_prep(P, q8, sf, s);
+    if (e != hipSuccess) return e;
+    L = LinArgs{q8, sf};
+  }
   EpiArgs E = {};
   E.out = out;
   E.ld = ld;
-  return dispatch_score<MODE_STORE>(P, E, tile_work(P, P.key_span, kChunkKeys), s);
+  return dispatch_score<MODE_STORE>(P, L, E, tile_work(P, P.key_span, kChunkKeys), s);
 }
 
 hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_idx, hipStream_t s, hipEvent_t* ev) {
@@ -626,6 +999,8 @@ hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_id
   hipError_t e;
   auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
   if ((e = mark(0)) != hipSuccess) return e;
+  const LinArgs L = lin_args(F);
+  if (!P.page_table && (e = launch_lin_prep(P, F.lin_q8, F.lin_sf, s)) != hipSuccess) return e;
   // K1a: samples
   {
     EpiArgs E = {};
@@ -634,7 +1009,7 @@ hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_id
     E.stride = F.stride;
     E.skip_le = F.cap;
     if (F.debug_mode != 0 && F.debug_row_mod <= 0) E.skip_le = 0x7FFFFFFF;  // every row forced
-    if ((e = dispatch_score<MODE_SAMPLE>(P, E, tile_work(P, F.ns, kChunkSamples), s)) != hipSuccess)
+    if ((e = dispatch_score<MODE_SAMPLE>(P, L, E, tile_work(P, F.ns, kChunkSamples), s)) != hipSuccess)
       return e;
     if ((e = mark(1)) != hipSuccess) return e;
   }
@@ -668,7 +1043,7 @@ hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_id
     E.slab_s = F.slab_s;
     E.slab_i = F.slab_i;
     E.cap = F.cap;
-    if ((e = dispatch_score<MODE_FILTER>(P, E, tile_work(P, P.key_span, kChunkKeys), s)) != hipSuccess)
+    if ((e = dispatch_score<MODE_FILTER>(P, L, E, tile_work(P, P.key_span, kChunkKeys), s)) != hipSuccess)
       return e;
     if ((e = mark(3)) != hipSuccess) return e;
   }
@@ -701,12 +1076,15 @@ hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_id
     B.out = out_idx;
     B.k = F.k;
     const dim3 grid(F.fb_blocks), block(kThreads);
-    if (P.fmt == FMT_E4M3) {
-      if (P.heads == 64) fallback_kernel<FMT_E4M3, 64><<<grid, block, 0, s>>>(A, B);
-      else fallback_kernel<FMT_E4M3, 32><<<grid, block, 0, s>>>(A, B);
+    if (P.page_table) {
+      if (P.heads == 64) fallback_paged_kernel<FMT_E4M3, 64><<<grid, block, 0, s>>>(A, B);
+      else fallback_paged_kernel<FMT_E4M3, 32><<<grid, block, 0, s>>>(A, B);
+    } else if (P.fmt == FMT_E4M3) {
+      if (P.heads == 64) fallback_tiles_kernel<FMT_E4M3, 64><<<grid, block, 0, s>>>(A, L, B);
+      else fallback_tiles_kernel<FMT_E4M3, 32><<<grid, block, 0, s>>>(A, L, B);
     } else {
-      if (P.heads == 64) fallback_kernel<FMT_MXFP4, 64><<<grid, block, 0, s>>>(A, B);
-      else fallback_kernel<FMT_MXFP4, 32><<<grid, block, 0, s>>>(A, B);
+      if (P.heads == 64) fallback_tiles_kernel<FMT_MXFP4, 64><<<grid, block, 0, s>>>(A, L, B);
+      else fallback_tiles_kernel<FMT_MXFP4, 32><<<grid, block, 0, s>>>(A, L, B);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(5)) != hipSuccess) return e;

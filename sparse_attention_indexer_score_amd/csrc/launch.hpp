@@ -39,11 +39,16 @@ struct FusedPlan {
   int32_t* slab_i;
   float* samp;
   float* scratch;
+  uint8_t* lin_q8;  // pieces of sum_h w_h q_h (contiguous keys)
+  uint8_t* lin_sf;
 };
 
 enum StatSlot { kStatStoreAll = 0, kStatSampled, kStatFallback, kStatMax, kStatMin, kStatTotal, kStatSlots = 8 };
 
-hipError_t launch_score_store(const DevProblem& P, float* out, int64_t ld, hipStream_t s);
+// ws: lin_ws_bytes(rows) bytes (contiguous keys; unused when paged).
+hipError_t launch_score_store(const DevProblem& P, float* out, int64_t ld, void* ws, hipStream_t s);
+size_t lin_ws_bytes(int32_t rows);
+void lin_carve(void* ws, int32_t rows, uint8_t** q8, uint8_t** sf);
 // ev: optional 6 events recorded at the stage boundaries (before K1a .. after K4).
 hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_idx, hipStream_t s,
                         hipEvent_t* ev = nullptr);

@@ -23,7 +23,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("idx_score", "idx_select", "idx_fused_topk", "idx_select_workspace", "idx_fused_workspace",
+    for n in ("idx_score", "idx_score_workspace", "idx_select", "idx_fused_topk", "idx_select_workspace",
+              "idx_fused_workspace",
               "idx_strerror", "idx_row_split", "idx_select_split", "idx_version"):
         assert n in names
 
@@ -89,7 +90,7 @@ def _problem(**kw):
 def test_problem_validation_on_host(mut, code):
     lib = sai.library()
     p = _problem(**mut)
-    assert lib.idx_score(ctypes.byref(p), ctypes.c_void_p(0x40000), 128, None) == code
+    assert lib.idx_score(ctypes.byref(p), ctypes.c_void_p(0x40000), 128, None, 0, None) == code
     assert lib.idx_fused_workspace(ctypes.byref(p), 16) == 0
 
 
@@ -98,7 +99,7 @@ def test_paged_mxfp4_is_a_format_error():
     p = _problem(fmt=sai.IDX_FMT_MXFP4, q_sf=ctypes.c_void_p(0x20000), k_sf=ctypes.c_void_p(0x20000),
                  page_table=ctypes.c_void_p(0x30000), row_req=ctypes.c_void_p(0x30000), num_req=1, max_pages=2,
                  num_keys=128)
-    assert lib.idx_score(ctypes.byref(p), ctypes.c_void_p(0x40000), 128, None) == sai.IDX_EFMT
+    assert lib.idx_score(ctypes.byref(p), ctypes.c_void_p(0x40000), 128, None, 0, None) == sai.IDX_EFMT
 
 
 def test_fused_argument_checks():
@@ -115,6 +116,20 @@ def test_fused_argument_checks():
     p0 = _problem(rows=0)
     assert lib.idx_fused_topk(ctypes.byref(p0), 16, None, None, 0, ctypes.byref(st), None) == 0
     assert st.cap == 64 and st.sample_stride == 1
+
+
+def test_score_workspace_and_check():
+    lib = sai.library()
+    p = _problem(rows=64, num_keys=4096)
+    need = lib.idx_score_workspace(ctypes.byref(p))
+    assert need >= 64 * 660
+    out = ctypes.c_void_p(0x40000)
+    assert lib.idx_score(ctypes.byref(p), out, 4096, None, 0, None) == sai.IDX_EWS
+    assert lib.idx_score(ctypes.byref(p), out, 4096, ctypes.c_void_p(0x100000), need - 1, None) == sai.IDX_EWS
+    assert lib.idx_score(ctypes.byref(p), out, 4096, ctypes.c_void_p(0x100080), need, None) == sai.IDX_EALIGN
+    paged = _problem(rows=4, page_table=ctypes.c_void_p(0x30000), row_req=ctypes.c_void_p(0x30000), num_req=1,
+                     max_pages=2, num_keys=128)
+    assert lib.idx_score_workspace(ctypes.byref(paged)) == 0
 
 
 def test_fused_workspace_grows_with_k_and_cap():
