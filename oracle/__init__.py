@@ -13,14 +13,15 @@ What it computes, and where that is defined
   sgl-project/sglang#47469, introduction).  The score is the MQA "logits" of
   DeepGEMM's ``mqa_logits`` (same page, introduction): per query head h a dot product
   of that head's query with the key's single shared vector, ReLU, then a sum over
-  heads weighted by the per-row head weight (same page, section 1: "every math thread
-  owns one key of the tile and reduces the heads in registers"):
+  heads weighted by the per-row head weight (same page, section 1: each thread of the
+  scoring tile holds one key and sums its heads in registers):
 
       score[r, s] = kscale[s] * sum_h w[r, h] * max(q[r, h] . k[s], 0)
 
   computed here in float64 from exactly decoded inputs and rounded once to fp32.
-* The top-k is exact (ROCm DSA indexer top-k page, sgl-project/sglang#37591, "fp32
-  coarse histogram" / "overflow rescan": recall 1.0 like torch.topk): order by fp32
+* The top-k is exact (ROCm DSA indexer top-k page, sgl-project/sglang#37591, code
+  analysis: an fp32 coarse histogram and a rescan on tie-buffer overflow give recall 1.0,
+  as torch.topk does): order by fp32
   value descending (-0.0 == +0.0), ties broken by the lower key index, keep
   min(k, visible) indices relative to the row's first visible key, pad with -1.
 * Paged K (LiteTopK page, section 3, topk_page_table_transform): logical position s of
