@@ -78,6 +78,84 @@ def cpu_baseline(p, rows_sample):
                       f"{dt:.1f} s"}
 
 
+def timed_ms(fn, iters, flush=None):
+    """Median and minimum HIP-event time of fn() on torch's current stream (the stream the
+    library launches on when given none).  flush() runs between iterations, outside the
+    timed region."""
+    import torch
+    marks = []
+    for _ in range(iters):
+        if flush is not None:
+            flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        marks.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in marks)
+    return ms[len(ms) // 2], ms[0]
+
+
+def secondary_legs(dev, iters=20):
+    """Selection (HBM-bound) and materialised scoring, measured beside the fused path:
+    idx_select on the selection workload (64 rows, pitch 131072) and on the prefill
+    workload's materialised scores (4096 x 65536 fp32, 1.04 GB), idx_score on prefill.
+    Cold numbers flush L2 and the 256 MB MALL with a 512 MiB fill before every call."""
+    import torch
+    import sparse_attention_indexer_score_amd as sai
+    from sparse_attention_indexer_score_amd import workloads as wl
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = lambda: flush_buf.fill_(0x5A)
+    res = {}
+
+    sp = wl.make("select")
+    x = torch.from_numpy(sp.x).to(dev)
+    length = torch.from_numpy(sp.length).to(dev)
+    run = sai.SelectRunner(x, length, sp.topk)
+    run()
+    torch.cuda.synchronize()
+    nbytes = int(sp.length.astype(np.int64).sum()) * 4 + x.shape[0] * sp.topk * 4
+    cold, cold_min = timed_ms(run, iters, flush)
+    warm, warm_min = timed_ms(run, iters)
+    res["select_workload"] = {
+        "what": "idx_select, 64 rows x pitch 131072, lengths U[2048, 131072], k=2048 (row split g=4)",
+        "bytes": nbytes, "cold_ms": round(cold, 4), "cold_min_ms": round(cold_min, 4),
+        "warm_ms": round(warm, 4), "cold_GBps": round(nbytes / (cold * 1e-3) / 1e9, 1),
+        "warm_GBps": round(nbytes / (warm * 1e-3) / 1e9, 1)}
+    log(f"[bench] select workload: cold {cold:.4f} ms, warm {warm:.4f} ms")
+    del x, length, run
+
+    pp = wl.make("prefill")
+    dpp = sai.DeviceProblem.from_host(pp, dev)
+    sr = sai.ScoreRunner(dpp, ld=int((pp.ke - pp.ks).max()))
+    sr()
+    torch.cuda.synchronize()
+    s_med, s_min = timed_ms(sr, 10)
+    pairs = pp.pairs
+    res["score_prefill"] = {
+        "what": "idx_score, prefill workload (4096 x 65536, e4m3, 64 heads): fp32 scores written",
+        "ms": round(s_med, 4), "min_ms": round(s_min, 4), "Gkey_scores_per_s": round(pairs / (s_med * 1e-3) / 1e9, 2),
+        "mfma_TFLOPs": round(pairs * 2 * 128 * pp.heads / (s_med * 1e-3) / 1e12, 1),
+        "write_GBps": round(pairs * 4 / (s_med * 1e-3) / 1e9, 1)}
+    log(f"[bench] idx_score prefill: {s_med:.4f} ms")
+    vlen = (dpp.ke - dpp.ks).to(torch.int32)
+    sel = sai.SelectRunner(sr.out, vlen, pp.topk)
+    sel()
+    torch.cuda.synchronize()
+    nbytes = int(pairs) * 4 + pp.rows * pp.topk * 4
+    cold, cold_min = timed_ms(sel, iters, flush)
+    res["select_prefill_materialised"] = {
+        "what": "idx_select over the prefill workload's materialised scores (4096 rows, 260,048,896 scores, k=2048)",
+        "bytes": nbytes, "cold_ms": round(cold, 4), "cold_min_ms": round(cold_min, 4),
+        "cold_GBps": round(nbytes / (cold * 1e-3) / 1e9, 1),
+        "hbm_frac": round(nbytes / (cold * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    log(f"[bench] select over materialised prefill scores: cold {cold:.4f} ms")
+    del sel, sr, dpp, flush_buf
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -85,6 +163,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-rows", type=int, default=16, help="rows in the oracle's timed sample (0: skip)")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the selection and materialised-score measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for HBM counters)")
     args = ap.parse_args()
@@ -152,6 +232,8 @@ def main():
     peak = PEAK_TFLOPS[p.fmt]
     traffic = load_traffic(args.workload, None)
 
+    secondary = None if args.no_secondary else secondary_legs(dev)
+
     cpu = None
     if args.cpu_rows > 0:
         step = max(1, p.rows // args.cpu_rows)
@@ -184,6 +266,7 @@ def main():
         "route": {kk: st[kk] for kk in ("rows_store_all", "rows_sampled", "fallback_rows", "max_count",
                                          "min_count", "total_count", "cap", "sample_stride")},
         "logits_bytes_avoided": int(pairs) * 4 * 2,
+        "secondary": secondary,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -233,6 +233,48 @@ def idx_select(scores: torch.Tensor, length: torch.Tensor, k: int, row_start: Op
     return out
 
 
+class SelectRunner:
+    """idx_select with a preallocated workspace and output (repeated calls allocate nothing)."""
+
+    def __init__(self, scores: torch.Tensor, length: torch.Tensor, k: int, row_start: Optional[torch.Tensor] = None,
+                 split: Optional[int] = None):
+        assert scores.dtype == torch.float32 and scores.dim() == 2 and scores.is_contiguous()
+        self.scores, self.length, self.k, self.row_start, self.split = scores, length, k, row_start, split
+        rows, ld = scores.shape
+        self.rows, self.ld = rows, ld
+        self.nbytes = idx_select_workspace(rows, ld, k)
+        self.ws = _workspace(self.nbytes, scores.device)
+        self.out = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
+
+    def __call__(self, stream=None) -> torch.Tensor:
+        L = _lib()
+        if self.split is None:
+            rc = L.idx_select(_ptr(self.scores), self.ld, _ptr(self.row_start), _ptr(self.length), self.rows, self.k,
+                              _ptr(self.out), _ptr(self.ws), self.nbytes, _stream(stream))
+        else:
+            rc = L.idx_select_split(_ptr(self.scores), self.ld, _ptr(self.row_start), _ptr(self.length), self.rows,
+                                    self.k, _ptr(self.out), _ptr(self.ws), self.nbytes, self.split, _stream(stream))
+        _check(rc, "idx_select")
+        return self.out
+
+
+class ScoreRunner:
+    """idx_score into a preallocated [rows, ld] buffer with a preallocated workspace."""
+
+    def __init__(self, prob: DeviceProblem, ld: Optional[int] = None):
+        self.prob = prob
+        self.s = prob.struct()
+        self.ld = ld if ld is not None else max(1, int((prob.ke - prob.ks).max().item()) if prob.rows else 1)
+        self.out = torch.empty((prob.rows, self.ld), dtype=torch.float32, device=prob.device)
+        self.nbytes = idx_score_workspace(prob)
+        self.ws = _workspace(self.nbytes, prob.device)
+
+    def __call__(self, stream=None) -> torch.Tensor:
+        _check(_lib().idx_score(ctypes.byref(self.s), _ptr(self.out), self.ld, _ptr(self.ws) if self.nbytes else None,
+                                self.nbytes, _stream(stream)), "idx_score")
+        return self.out
+
+
 # ----------------------------------------------------------------------------- fused top-k
 
 def idx_fused_workspace(prob: DeviceProblem, k: int) -> int:

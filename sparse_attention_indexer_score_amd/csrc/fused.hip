@@ -31,7 +31,7 @@ constexpr int kTile = 32;      // keys per MFMA block
 
 // Rows per workgroup: 4 waves x 2 rows (contiguous kernel); the paged kernel holds 4 rows
 // per wave at 32 heads.
-int rows_per_block(int heads) { return 8; }
+int rows_per_block(int heads) { return 4 * (heads == 32 ? 4 : 2); }
 static int rows_per_block_paged(int heads) { return 4 * (heads == 64 ? 2 : 4); }
 static int rows_per_block_for(const DevProblem& P) {
   return P.page_table ? rows_per_block_paged(P.heads) : rows_per_block(P.heads);
@@ -246,10 +246,11 @@ constexpr int kPieces = 5;
 constexpr int kLinRowBytes = kPieces * 2 * 2 * 32;  // pieces x ksteps x halves x 32 bytes (24 used)
 constexpr int kLinRowScales = kPieces * 2 * 2;
 
-// Rows per wave of the contiguous kernel (register budget of the pipelined tile loop).
+// Rows per wave of the contiguous kernel: 4 at 32 heads (the linear tile then serves 4 rows
+// and every key operand read from LDS feeds 8 MFMAs), 2 at 64 heads (register budget).
 template <int H>
 struct RowsPerWave {
-  static constexpr int value = 2;
+  static constexpr int value = H == 32 ? 4 : 2;
 };
 
 struct LinArgs {
@@ -469,7 +470,14 @@ struct StageLds {
   uint8_t* codes;  // [2][kKeys * kStride]
   uint32_t* sf;    // [2][kKeys] e8m0 words (MXFP4)
   float* ks;       // [2][kKeys] per-key scale (1.0 when absent)
+  float* cand_s;   // FILTER: [waves][RW][kCandBuf] candidate scores of this workgroup's rows
+  int32_t* cand_i; //         and their key indices relative to ks
 };
+
+// FILTER mode: each wave collects the candidates of its own rows in LDS (no atomics: the
+// rows are the wave's alone) and moves them to the global slab in batches, with one
+// global atomic per row and batch instead of one per tile.
+constexpr int kCandBuf = 256;
 
 // Scores of the RW rows [row0, row0 + RW) of this wave on the workgroup's tiles [tA, tB)
 // (positions: keys, or sample slots with key = phase + pos * S), with the epilogue of MODE.
@@ -540,6 +548,36 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
     return key < last_key ? key : last_key;
   };
 
+  // FILTER: this wave's LDS candidate buffers and their (wave-uniform) fill counts.
+  float* cs = MODE == MODE_FILTER ? sl.cand_s + wave * RW * kCandBuf : nullptr;
+  int32_t* ci = MODE == MODE_FILTER ? sl.cand_i + wave * RW * kCandBuf : nullptr;
+  int ccnt[RW];
+#pragma unroll
+  for (int i = 0; i < RW; ++i) ccnt[i] = 0;
+  // Move row i's buffered candidates to the slab: one atomic reserves the slots; slots at
+  // or past cap are dropped but still counted (the count then flags the overflow).
+  auto flush = [&](int i) {
+    const int n = ccnt[i];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int base = 0;
+    if (l == 0) base = atomicAdd(&E.cnt[row0 + i], n);
+    base = readlane(base, 0);
+    const int64_t row_off = (int64_t)(row0 + i) * E.cap;
+    for (int j = l; j < n; j += kWave) {
+      const int slot = base + j;
+      if (slot < E.cap) {
+        E.slab_s[row_off + slot] = cs[i * kCandBuf + j];
+        E.slab_i[row_off + slot] = ci[i * kCandBuf + j];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    ccnt[i] = 0;
+  };
+
   // Epilogue of one tile for every row pair, given the pairs' packed scores.
   auto epilogue = [&](int t, const float* score_of) {
     const int pos = t * kTile + col;
@@ -558,19 +596,19 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
       } else {
         const bool pred = valid && score >= thr_l[p];
         const uint64_t m = wave_ballot(pred);
-        if (m) {
-          const uint32_t mA = (uint32_t)m, mB = (uint32_t)(m >> 32);
-          int baseA = 0, baseB = 0;
-          if (l == 0 && mA) baseA = atomicAdd(&E.cnt[row0 + 2 * p], __builtin_popcount(mA));
-          if (l == 32 && mB) baseB = atomicAdd(&E.cnt[row0 + 2 * p + 1], __builtin_popcount(mB));
-          baseA = readlane(baseA, 0);
-          baseB = readlane(baseB, 32);
-          const int slot = (half ? baseB : baseA) + mask_prefix(m) - (half ? __builtin_popcount(mA) : 0);
-          if (pred && slot < E.cap) {
-            const int64_t o = row_l[p] * E.cap + slot;
-            E.slab_s[o] = score;
-            E.slab_i[o] = (int32_t)(key - ks_l[p]);
+        if (m) {  // wave-uniform
+          const int nA = __builtin_popcountll(m & 0xFFFFFFFFull), nB = __builtin_popcountll(m >> 32);
+          const int slot = (half ? ccnt[2 * p + 1] - nA : ccnt[2 * p]) + mask_prefix(m);
+          if (pred) {
+            const int o = (2 * p + half) * kCandBuf + slot;
+            cs[o] = score;
+            ci[o] = (int32_t)(key - ks_l[p]);
           }
+          ccnt[2 * p] += nA;
+          ccnt[2 * p + 1] += nB;
+          // A row gains at most kTile candidates per tile: flush before the next could overflow.
+          if (ccnt[2 * p] > kCandBuf - kTile) flush(2 * p);
+          if (ccnt[2 * p + 1] > kCandBuf - kTile) flush(2 * p + 1);
         }
       }
     }
@@ -679,6 +717,11 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
     if (more) lwrite(buf ^ 1);
     __syncthreads();
   }
+  if constexpr (MODE == MODE_FILTER) {
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+      if (ccnt[i] > 0) flush(i);
+  }
 }
 
 template <int FMT>
@@ -688,10 +731,23 @@ struct StageShared {
   float ks[2 * StageGeom<FMT>::kKeys];
 };
 
+// Candidate buffers of the 4 waves (FILTER mode only).
+template <int RW, bool ON>
+struct CandShared {
+  float s[4 * RW * kCandBuf];
+  int32_t i[4 * RW * kCandBuf];
+};
+template <int RW>
+struct CandShared<RW, false> {
+  float s[1];
+  int32_t i[1];
+};
+
 template <int FMT, int H, int MODE>
-__global__ __launch_bounds__(kThreads) void score_tiles_kernel(ScoreArgs A, LinArgs L, EpiArgs E, TileWork W) {
+__global__ __launch_bounds__(kThreads, 2) void score_tiles_kernel(ScoreArgs A, LinArgs L, EpiArgs E, TileWork W) {
   constexpr int RW = RowsPerWave<H>::value;
   __shared__ StageShared<FMT> sh;
+  __shared__ CandShared<RW, MODE == MODE_FILTER> cand;
   const int64_t item = map_item(W);
   if (item >= W.total) return;
   const int rb = (int)(item % W.nrb);
@@ -716,7 +772,7 @@ __global__ __launch_bounds__(kThreads) void score_tiles_kernel(ScoreArgs A, LinA
   }
   const int tA = max(c0, lo) / kTile, tB = (min(c1, hi) + kTile - 1) / kTile;
   if (tA >= tB) return;  // workgroup-uniform
-  const StageLds<FMT> sl{sh.codes, sh.sf, sh.ks};
+  const StageLds<FMT> sl{sh.codes, sh.sf, sh.ks, cand.s, cand.i};
   wg_tiles<FMT, H, MODE, RW, false>(A, L, E, rb * 4 * RW + wave * RW, phase, S, c0, c1, tA, tB, sl);
 }
 
@@ -858,12 +914,15 @@ __global__ __launch_bounds__(kThreads) void fallback_paged_kernel(ScoreArgs A, F
 }
 
 
-// Contiguous keys: the row is re-scored by wg_tiles() for the same pair of rows, tiles and
-// lane positions as in score_tiles_kernel (each wave takes one tile of every stage), so its
-// scores are bitwise the ones the slab was filtered with; only the row itself is stored.
+// Contiguous keys: the row is re-scored by wg_tiles() with the same tiles and lane positions
+// as in score_tiles_kernel (each wave takes one tile of every stage).  A row's score does
+// not depend on which rows share its wave: its MFMA outputs, its head reduce, the half-wave
+// sum (low half + high half) and its linear-tile pieces are computed the same way for any
+// pairing, so the scores are bitwise the ones the slab was filtered with.  Only the row
+// itself is stored; 2 rows per wave keep the register budget of this LDS-heavy kernel.
 template <int FMT, int H>
 __global__ __launch_bounds__(kThreads) void fallback_tiles_kernel(ScoreArgs A, LinArgs L, FbArgs F) {
-  constexpr int RW = RowsPerWave<H>::value;
+  constexpr int RW = 2;
   __shared__ SelSmem sm;
   __shared__ StageShared<FMT> sh;
   __shared__ int sh_item;
