@@ -29,12 +29,12 @@ enum : int { MODE_STORE = 0, MODE_FILTER = 1, MODE_SAMPLE = 2, MODE_ROWSTORE = 3
 constexpr int kThreads = 256;  // 4 waves per workgroup
 constexpr int kTile = 32;      // keys per MFMA block
 
-// Rows per workgroup: 4 waves x 2 rows (contiguous kernel); the paged kernel holds 4 rows
-// per wave at 32 heads.
-int rows_per_block(int heads) { return 4 * (heads == 32 ? 4 : 2); }
+// Rows per workgroup: 4 waves x RowsPerWave (contiguous kernel: 4 rows per wave for MXFP4
+// at 32 heads, else 2); the paged kernel holds 4 rows per wave at 32 heads.
+int rows_per_block(int heads, int fmt) { return 4 * (heads == 32 && fmt == FMT_MXFP4 ? 4 : 2); }
 static int rows_per_block_paged(int heads) { return 4 * (heads == 64 ? 2 : 4); }
 static int rows_per_block_for(const DevProblem& P) {
-  return P.page_table ? rows_per_block_paged(P.heads) : rows_per_block(P.heads);
+  return P.page_table ? rows_per_block_paged(P.heads) : rows_per_block(P.heads, P.fmt);
 }
 
 // Odd sample stride: the largest odd S <= 2.25*k/64, so that a row of V keys yields about
@@ -246,11 +246,12 @@ constexpr int kPieces = 5;
 constexpr int kLinRowBytes = kPieces * 2 * 2 * 32;  // pieces x ksteps x halves x 32 bytes (24 used)
 constexpr int kLinRowScales = kPieces * 2 * 2;
 
-// Rows per wave of the contiguous kernel: 4 at 32 heads (the linear tile then serves 4 rows
-// and every key operand read from LDS feeds 8 MFMAs), 2 at 64 heads (register budget).
-template <int H>
+// Rows per wave of the contiguous kernel: 4 for MXFP4 at 32 heads (the linear tile then
+// serves 4 rows and every key operand read from LDS feeds 8 MFMAs), otherwise 2 (register
+// budget: e4m3 operands are twice as wide, 64 heads twice as many).
+template <int FMT, int H>
 struct RowsPerWave {
-  static constexpr int value = H == 32 ? 4 : 2;
+  static constexpr int value = (FMT == FMT_MXFP4 && H == 32) ? 4 : 2;
 };
 
 struct LinArgs {
@@ -384,17 +385,6 @@ __device__ __forceinline__ void mfma_row(v16f (&acc)[H / 32], const RowOperand<F
   }
 }
 
-// Per-lane partial of sum_h w_h |x_h| over the heads this lane holds.
-template <int FMT, int H>
-__device__ __forceinline__ float reduce_abs(const v16f (&acc)[H / 32], const RowOperand<FMT, H>& ro) {
-  float p = 0.0f;
-#pragma unroll
-  for (int mt = 0; mt < H / 32; ++mt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) p = __builtin_fmaf(ro.w[mt][i], __builtin_fabsf(acc[mt][i]), p);
-  return p;
-}
-
 // Pieces of up to three row pairs of a wave as the A operand of the linear MFMA: lane l
 // supplies M row (l % 32) = 8g + 4hh + j, slot s = 4g + j holds piece (s % 5) of row
 // row0 + 2 (s / 5) + hh.  In the result, lane half H then holds in accumulator s the
@@ -443,25 +433,27 @@ __device__ __forceinline__ float lin_of_pair(const v16f& a, int p) {
   return x;
 }
 
-__device__ __forceinline__ float finish_score2(float abs_sum, float lin, float kscale) {
-  return ((lin + abs_sum) * 0.5f) * kscale;
+// score = kscale * (lin + abs_sum) / 2, given half_kscale = kscale / 2 (exact: a power-of-two
+// factor moves freely between the two products while nothing underflows).
+__device__ __forceinline__ float finish_score2(float abs_sum, float lin, float half_kscale) {
+  return (lin + abs_sum) * half_kscale;
 }
 
 // Key tiles are staged through LDS: all four waves of a workgroup use the same keys, so a
-// stage of kStageTiles 32-key tiles is fetched once per workgroup with coalesced 16-byte
-// loads (issued one stage ahead, double-buffered, one barrier per stage) and each wave
-// reads its MFMA key operands from LDS.  Rows are padded to KB + 16 bytes so that the 8
-// lanes of a 16-byte LDS read phase hit distinct banks.
-constexpr int kStageTiles = 4;
-
+// stage of 32-key tiles is fetched once per workgroup with coalesced 16-byte loads (issued
+// one stage ahead, double-buffered, one barrier per stage) and each wave reads its MFMA key
+// operands from LDS.  Rows are padded to KB + 16 bytes so that the 8 lanes of a 16-byte LDS
+// read phase hit distinct banks.  A stage is 8 tiles of 80-byte fp4 rows or 4 tiles of
+// 144-byte e4m3 rows, which keeps two workgroups per CU within LDS.
 template <int FMT>
 struct StageGeom {
+  static constexpr int kTiles = FMT == FMT_MXFP4 ? 8 : 4;  // tiles per stage
   static constexpr int kKB = Fmt<FMT>::kBytes;
   static constexpr int kStride = kKB + 16;
-  static constexpr int kKeys = kStageTiles * kTile;        // 128 keys per stage
+  static constexpr int kKeys = kTiles * kTile;             // keys per stage
   static constexpr int kBytes = kKeys * kStride;           // codes of one stage
   static constexpr int kChunks = kKeys * kKB / 16;          // 16-byte loads per stage
-  static constexpr int kPerThread = kChunks / kThreads;     // fp4: 2, fp8: 4
+  static constexpr int kPerThread = kChunks / kThreads;     // fp4: 4, fp8: 4
   static_assert(kChunks % kThreads == 0, "stage must split evenly");
 };
 
@@ -469,7 +461,7 @@ template <int FMT>
 struct StageLds {
   uint8_t* codes;  // [2][kKeys * kStride]
   uint32_t* sf;    // [2][kKeys] e8m0 words (MXFP4)
-  float* ks;       // [2][kKeys] per-key scale (1.0 when absent)
+  float* ks;       // [2][kKeys] half the per-key scale (0.5 when absent)
   float* cand_s;   // FILTER: [waves][RW][kCandBuf] candidate scores of this workgroup's rows
   int32_t* cand_i; //         and their key indices relative to ks
 };
@@ -483,7 +475,7 @@ constexpr int kCandBuf = 256;
 // (positions: keys, or sample slots with key = phase + pos * S), with the epilogue of MODE.
 // Every wave of the workgroup must call it with the same tA, tB.  MAIN mode: every wave
 // scores every tile that meets its rows.  FALLBACK mode: all waves hold the same rows and
-// wave w scores tile w of each stage; MODE_ROWSTORE then writes only row E.only_row, to
+// wave w scores tiles w and w + 4 of each stage; MODE_ROWSTORE then writes only row E.only_row, to
 // E.out[key - ks].
 template <int FMT, int H, int MODE, int RW, bool FALLBACK>
 __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, const EpiArgs& E, int row0,
@@ -583,25 +575,30 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
     const int pos = t * kTile + col;
     const int64_t key = (int64_t)phase + (int64_t)pos * S;
     const bool full = t * kTile >= full_lo && (t + 1) * kTile <= full_hi;  // wave-uniform
+    if constexpr (MODE == MODE_FILTER) {
+      // One compare and ballot per row pair; the append path runs only for the (rare)
+      // tiles that hold a candidate.
+      uint64_t m[NP];
+      uint64_t any = 0;
+      if (full) {
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const float score = score_of[p];
-      const bool valid = full || (pos >= lo_l[p] && pos < hi_l[p]);
-      if constexpr (MODE == MODE_STORE) {
-        if (valid) E.out[row_l[p] * E.ld + (key - ks_l[p])] = score;
-      } else if constexpr (MODE == MODE_ROWSTORE) {
-        if (valid && row_l[p] == E.only_row) E.out[key - ks_l[p]] = score;
-      } else if constexpr (MODE == MODE_SAMPLE) {
-        if (valid) E.samp[row_l[p] * E.ns + pos] = score;
+        for (int p = 0; p < NP; ++p) m[p] = wave_ballot(score_of[p] >= thr_l[p]);
       } else {
-        const bool pred = valid && score >= thr_l[p];
-        const uint64_t m = wave_ballot(pred);
-        if (m) {  // wave-uniform
-          const int nA = __builtin_popcountll(m & 0xFFFFFFFFull), nB = __builtin_popcountll(m >> 32);
-          const int slot = (half ? ccnt[2 * p + 1] - nA : ccnt[2 * p]) + mask_prefix(m);
-          if (pred) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+          m[p] = wave_ballot(pos >= lo_l[p] && pos < hi_l[p] && score_of[p] >= thr_l[p]);
+      }
+#pragma unroll
+      for (int p = 0; p < NP; ++p) any |= m[p];
+      if (any) {  // wave-uniform
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          if (!m[p]) continue;  // wave-uniform
+          const int nA = __builtin_popcountll(m[p] & 0xFFFFFFFFull), nB = __builtin_popcountll(m[p] >> 32);
+          if ((m[p] >> l) & 1) {
+            const int slot = (half ? ccnt[2 * p + 1] - nA : ccnt[2 * p]) + mask_prefix(m[p]);
             const int o = (2 * p + half) * kCandBuf + slot;
-            cs[o] = score;
+            cs[o] = score_of[p];
             ci[o] = (int32_t)(key - ks_l[p]);
           }
           ccnt[2 * p] += nA;
@@ -611,11 +608,25 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
           if (ccnt[2 * p + 1] > kCandBuf - kTile) flush(2 * p + 1);
         }
       }
+    } else {
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const float score = score_of[p];
+        const bool valid = full || (pos >= lo_l[p] && pos < hi_l[p]);
+        if constexpr (MODE == MODE_STORE) {
+          if (valid) E.out[row_l[p] * E.ld + (key - ks_l[p])] = score;
+        } else if constexpr (MODE == MODE_ROWSTORE) {
+          if (valid && row_l[p] == E.only_row) E.out[key - ks_l[p]] = score;
+        } else {
+          if (valid) E.samp[row_l[p] * E.ns + pos] = score;
+        }
+      }
     }
   };
 
-  // Key operand and key scale of tile slot i of LDS stage buffer `buf`.
-  auto read_b = [&](int buf, int i, KeyOperand& ko, float& kscale) {
+
+  // Key operand and half key scale of tile slot i of LDS stage buffer `buf`.
+  auto read_b = [&](int buf, int i, KeyOperand& ko, float& half_kscale) {
     const int kidx = i * kTile + col;
     const uint8_t* row = sl.codes + buf * G::kBytes + kidx * G::kStride;
 #pragma unroll
@@ -635,7 +646,7 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
       ko.sb[0] = (sw >> (8 * half)) & 0xFF;
       ko.sb[1] = (sw >> (8 * (2 + half))) & 0xFF;
     }
-    kscale = sl.ks[buf * G::kKeys + kidx];
+    half_kscale = sl.ks[buf * G::kKeys + kidx];
   };
   struct Acc {
     v16f row[RW][H / 32];
@@ -646,13 +657,32 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
 #pragma unroll
     for (int r = 0; r < RW; ++r) mfma_row<FMT, H>(a.row[r], ro[r], ko);
   };
-  auto reduce = [&](const Acc& a, float kscale, float* sc) {
+  // Head reduce of all RW rows; at 4 rows per wave the rows' chains are interleaved for
+  // instruction-level parallelism.  Each row's own sum runs over its heads in one fixed order.
+  auto reduce = [&](const Acc& a, float half_kscale, float* sc) {
+    float part[RW];
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const float pa = reduce_abs<FMT, H>(a.row[2 * p], ro[2 * p]);
-      const float pb = reduce_abs<FMT, H>(a.row[2 * p + 1], ro[2 * p + 1]);
-      sc[p] = finish_score2(combine_halves(pa, pb), lin_of_pair(a.lin, p), kscale);
+    for (int r = 0; r < RW; ++r) part[r] = 0.0f;
+    if constexpr (RW >= 4) {
+#pragma unroll
+      for (int mt = 0; mt < H / 32; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+#pragma unroll
+          for (int r = 0; r < RW; ++r)
+            part[r] = __builtin_fmaf(ro[r].w[mt][i], __builtin_fabsf(a.row[r][mt][i]), part[r]);
+    } else {  // same sums, row after row (fewer live registers)
+#pragma unroll
+      for (int r = 0; r < RW; ++r)
+#pragma unroll
+        for (int mt = 0; mt < H / 32; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            part[r] = __builtin_fmaf(ro[r].w[mt][i], __builtin_fabsf(a.row[r][mt][i]), part[r]);
     }
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+      sc[p] = finish_score2(combine_halves(part[2 * p], part[2 * p + 1]), lin_of_pair(a.lin, p), half_kscale);
   };
   // One tile: key operand from LDS, MFMAs for all RW rows and the linear tile, reduce, epilogue.
   auto compute = [&](int buf, int i, int t) {
@@ -672,7 +702,7 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
   uint32_t sfw = 0;
   float ksv = 1.0f;
   auto gload = [&](int stage) {
-    const int64_t pos0 = (int64_t)(tA + stage * kStageTiles) * kTile;
+    const int64_t pos0 = (int64_t)(tA + stage * G::kTiles) * kTile;
 #pragma unroll
     for (int u = 0; u < G::kPerThread; ++u) {
       const int c = threadIdx.x + u * kThreads;
@@ -694,11 +724,11 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
     }
     if (threadIdx.x < G::kKeys) {
       sl.sf[buf * G::kKeys + threadIdx.x] = sfw;
-      sl.ks[buf * G::kKeys + threadIdx.x] = ksv;
+      sl.ks[buf * G::kKeys + threadIdx.x] = 0.5f * ksv;
     }
   };
 
-  const int nst = (tB - tA + kStageTiles - 1) / kStageTiles;
+  const int nst = (tB - tA + G::kTiles - 1) / G::kTiles;
   gload(0);
   lwrite(0);
   __syncthreads();
@@ -706,12 +736,12 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
     const int buf = st & 1;
     const bool more = st + 1 < nst;
     if (more) gload(st + 1);
-    const int tbase = tA + st * kStageTiles;
+    const int tbase = tA + st * G::kTiles;
 #pragma unroll
-    for (int i = 0; i < kStageTiles; ++i) {
+    for (int i = 0; i < G::kTiles; ++i) {
       const int t = tbase + i;
       if (t >= tB) break;  // workgroup-uniform
-      const bool mine = FALLBACK ? (i == wave) : (t >= wt0 && t < wt1);
+      const bool mine = FALLBACK ? ((i & 3) == wave) : (t >= wt0 && t < wt1);
       if (mine) compute(buf, i, t);
     }
     if (more) lwrite(buf ^ 1);
@@ -745,7 +775,7 @@ struct CandShared<RW, false> {
 
 template <int FMT, int H, int MODE>
 __global__ __launch_bounds__(kThreads, 2) void score_tiles_kernel(ScoreArgs A, LinArgs L, EpiArgs E, TileWork W) {
-  constexpr int RW = RowsPerWave<H>::value;
+  constexpr int RW = RowsPerWave<FMT, H>::value;
   __shared__ StageShared<FMT> sh;
   __shared__ CandShared<RW, MODE == MODE_FILTER> cand;
   const int64_t item = map_item(W);
@@ -915,7 +945,7 @@ __global__ __launch_bounds__(kThreads) void fallback_paged_kernel(ScoreArgs A, F
 
 
 // Contiguous keys: the row is re-scored by wg_tiles() with the same tiles and lane positions
-// as in score_tiles_kernel (each wave takes one tile of every stage).  A row's score does
+// as in score_tiles_kernel (each wave takes two tiles of every stage).  A row's score does
 // not depend on which rows share its wave: its MFMA outputs, its head reduce, the half-wave
 // sum (low half + high half) and its linear-tile pieces are computed the same way for any
 // pairing, so the scores are bitwise the ones the slab was filtered with.  Only the row
@@ -1024,7 +1054,15 @@ static hipError_t dispatch_score(const DevProblem& P, const LinArgs& L, const Ep
   return hipGetLastError();
 }
 
-constexpr int kChunkKeys = 4096;
+// Keys per work item of the score kernels: long enough to amortise a workgroup's row
+// operand loads (up to 16384), short enough that the grid keeps about 8192 workgroups.
+static int chunk_keys(const DevProblem& P) {
+  const int rb = rows_per_block_for(P);
+  const int64_t nrb = (P.rows + rb - 1) / rb;
+  int64_t c = (std::max<int64_t>(P.key_span, 1) * nrb + 8191) / 8192;
+  c = (c + 4095) / 4096 * 4096;
+  return (int)std::min<int64_t>(std::max<int64_t>(c, 4096), 16384);
+}
 constexpr int kChunkSamples = 1024;
 
 size_t lin_ws_bytes(int32_t rows) {
@@ -1050,7 +1088,7 @@ hipError_t launch_score_store(const DevProblem& P, float* out, int64_t ld, void*
   EpiArgs E = {};
   E.out = out;
   E.ld = ld;
-  return dispatch_score<MODE_STORE>(P, L, E, tile_work(P, P.key_span, kChunkKeys), s);
+  return dispatch_score<MODE_STORE>(P, L, E, tile_work(P, P.key_span, chunk_keys(P)), s);
 }
 
 hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_idx, hipStream_t s, hipEvent_t* ev) {
@@ -1102,7 +1140,7 @@ hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_id
     E.slab_s = F.slab_s;
     E.slab_i = F.slab_i;
     E.cap = F.cap;
-    if ((e = dispatch_score<MODE_FILTER>(P, L, E, tile_work(P, P.key_span, kChunkKeys), s)) != hipSuccess)
+    if ((e = dispatch_score<MODE_FILTER>(P, L, E, tile_work(P, P.key_span, chunk_keys(P)), s)) != hipSuccess)
       return e;
     if ((e = mark(3)) != hipSuccess) return e;
   }

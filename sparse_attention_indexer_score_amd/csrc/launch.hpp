@@ -60,7 +60,7 @@ hipError_t launch_select_split(const float* x, int64_t ld, const int32_t* row_st
 size_t select_split_ws_bytes(int32_t rows);
 
 // Score-kernel work decomposition shared with the host sizing code.
-int rows_per_block(int heads);
+int rows_per_block(int heads, int fmt);
 int sample_stride_for(int k);  // odd stride S
 
 }  // namespace idx
