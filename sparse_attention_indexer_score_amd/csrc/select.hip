@@ -3,7 +3,9 @@
 // ROCm DSA indexer top-k page (sgl-project/sglang#37591): fp32 radix histogram of 12
 // bits, exact tie refinement, full-row rescan when the tie buffer overflows, and, for
 // long rows at low batch, several workgroups per row ("row split"):
-//   split == 0  select_rows_kernel: one 1024-thread workgroup per row (block_select)
+//   split == 0  select_rows_kernel: one 1024-thread workgroup per row (a sampled threshold,
+//               one pass into an LDS candidate buffer, radix refinement in LDS; the
+//               multi-pass block_select when the sample misjudges the row)
 //   split >= 2  mb_hist_kernel    g workgroups per row add their segment's level-1
 //                                 histogram into a per-row global histogram
 //               mb_scatter_kernel every workgroup finds the boundary bin from it, writes
@@ -18,16 +20,25 @@ namespace idx {
 
 constexpr int kSelThreads = 1024;
 
-__global__ __launch_bounds__(kSelThreads) void select_rows_kernel(const float* x, int64_t ld,
+// Candidate buffer of the single-workgroup path: 6144 (key, index) pairs, 64 KB of LDS with
+// the histogram; with at most 64 VGPRs (8 waves per SIMD) two 1024-thread workgroups fit on
+// a CU.
+constexpr int kSelCand = 6144;
+
+__global__ __launch_bounds__(kSelThreads, 8) void select_rows_kernel(const float* x, int64_t ld,
                                                                   const int32_t* row_start, const int32_t* len,
                                                                   int32_t k, int32_t* out) {
-  __shared__ SelSmem sm;
+  __shared__ SelSmemT<kSelCand> sm;
   const int r = blockIdx.x;
   const int n = len[r];
   const int64_t off = (int64_t)r * ld + (row_start ? row_start[r] : 0);
   const int m = min(k, n);
   int32_t* o = out + (int64_t)r * k;
-  if (m > 0) block_select<kSelThreads>(RowSrc{x + off}, n, m, o, sm);
+  if (m >= n) {
+    for (int j = threadIdx.x; j < n; j += kSelThreads) o[j] = j;
+  } else if (m > 0) {
+    block_select_sampled<kSelThreads>(x + off, n, m, o, sm);
+  }
   for (int j = m + threadIdx.x; j < k; j += kSelThreads) o[j] = -1;
 }
 

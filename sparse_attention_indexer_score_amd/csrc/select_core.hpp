@@ -10,11 +10,14 @@
 //   level 1  an LDS histogram of the top 12 value bits over the whole input;
 //   boundary the bin where the count from the top reaches m;
 //   then     elements above the boundary bin are selected, elements inside it go to an
-//            LDS tie buffer (kTieCap entries) and are refined by the next levels in LDS;
-//            if the bin holds more than kTieCap elements the next levels rescan the
+//            LDS tie buffer (SM::kCap entries) and are refined by the next levels in LDS;
+//            if the bin holds more than SM::kCap elements the next levels rescan the
 //            input instead, keeping only elements whose higher digits match.
-// Selection stops at the first level whose boundary bin is entirely selected.
+// Selection stops at the first level whose boundary bin is entirely selected, or once the
+// bin holds at most 64 elements, which one wave then ranks directly.
 #pragma once
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace idx {
@@ -39,17 +42,22 @@ __device__ __forceinline__ uint64_t composite_key(uint32_t okey, int32_t index) 
   return ((uint64_t)okey << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)index);
 }
 
-struct SelSmem {
+// LDS of one selecting workgroup; CAP is the capacity of the tie / candidate buffer.
+template <int CAP>
+struct SelSmemT {
+  static constexpr int kCap = CAP;
   uint32_t hist[kHistBins];
-  uint32_t tkey[kTieCap];
-  int32_t tidx[kTieCap];
+  uint32_t tkey[CAP];
+  int32_t tidx[CAP];
   uint32_t scan[20];
   int32_t nout;
   int32_t ntie;
   int32_t bnd_bin;
   uint32_t bnd_above;
   uint32_t bnd_count;
+  uint32_t kmin, kmax;
 };
+using SelSmem = SelSmemT<kTieCap>;
 
 // Input sources: element j has an order key and an index.
 struct RowSrc {  // materialised fp32 row, index = position
@@ -57,6 +65,37 @@ struct RowSrc {  // materialised fp32 row, index = position
   __device__ __forceinline__ uint32_t key(int j) const { return order_key(x[j]); }
   __device__ __forceinline__ int32_t index(int j) const { return j; }
 };
+struct LdsKeySrc {  // order keys already in LDS, index = position
+  const uint32_t* k;
+  __device__ __forceinline__ uint32_t key(int j) const { return k[j]; }
+  __device__ __forceinline__ int32_t index(int j) const { return j; }
+};
+
+// Order-preserving normalisation of keys known to lie in [lo, hi]: (key - lo) << lz with
+// lz = the leading zeros of hi - lo, so that the keys' first differing bit becomes the top
+// bit and a 12-bit histogram of the result spreads them over its bins (raw order keys of
+// scores with one common exponent fall into a handful of bins).  Injective, and inverted
+// by denormalize() for keys of the form normalize(k).
+struct KeyNorm {
+  uint32_t lo;
+  int lz;  // 32 when hi == lo: every key maps to 0
+  __device__ __forceinline__ uint32_t normalize(uint32_t k) const { return lz >= 32 ? 0u : (k - lo) << lz; }
+  __device__ __forceinline__ uint32_t denormalize(uint32_t v) const { return lz >= 32 ? lo : (v >> lz) + lo; }
+};
+__device__ __forceinline__ KeyNorm key_norm(uint32_t lo, uint32_t hi) {
+  return KeyNorm{lo, hi == lo ? 32 : __builtin_clz(hi - lo)};
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, d, kWave));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) v = min(v, (uint32_t)__shfl_xor((int)v, d, kWave));
+  return v;
+}
 struct PairSrc {  // (score, index) pairs, e.g. a candidate slab row
   const float* s;
   const int32_t* i;
@@ -64,15 +103,15 @@ struct PairSrc {  // (score, index) pairs, e.g. a candidate slab row
   __device__ __forceinline__ int32_t index(int j) const { return i[j]; }
 };
 
-template <int NT>
-__device__ __forceinline__ void zero_hist(SelSmem& sm, int nbins) {
+template <int NT, class SM>
+__device__ __forceinline__ void zero_hist(SM& sm, int nbins) {
   for (int b = threadIdx.x; b < nbins; b += NT) sm.hist[b] = 0;
 }
 
 // Largest bin b with (count of bins >= b) >= need; need >= 1 and the total must reach it.
 // Results in sm.bnd_*.  Contains barriers.
-template <int NT>
-__device__ void find_boundary(SelSmem& sm, int nbins, uint32_t need) {
+template <int NT, class SM>
+__device__ void find_boundary(SM& sm, int nbins, uint32_t need) {
   const int per = (nbins + NT - 1) / NT;
   const int hi = nbins - (int)threadIdx.x * per;  // this thread covers [lo, hi), high bins first
   const int lo = hi - per < 0 ? 0 : hi - per;
@@ -108,8 +147,8 @@ __device__ __forceinline__ int wave_append_slot(bool pred, int32_t* counter) {
 }
 
 // Emit every element whose composite key has (K >> shift) >= prefix (shift <= 52).
-template <int NT, class Src>
-__device__ void emit_at_least(const Src& src, int n, int shift, uint64_t prefix, int32_t* out, SelSmem& sm) {
+template <int NT, class Src, class SM>
+__device__ void emit_at_least(const Src& src, int n, int shift, uint64_t prefix, int32_t* out, SM& sm) {
   for (int base = 0; base < n; base += NT) {
     const int j = base + (int)threadIdx.x;
     bool take = false;
@@ -125,9 +164,9 @@ __device__ void emit_at_least(const Src& src, int n, int shift, uint64_t prefix,
 
 // Refine the LDS tie list (sm.ntie entries, all sharing the digits above level L) until
 // `need` more elements are emitted to out[] through sm.nout.  Contains barriers.
-template <int NT>
-__device__ void refine_lds(int L, uint32_t need, int32_t* out, SelSmem& sm) {
-  constexpr int PER = kTieCap / NT;
+template <int NT, class SM>
+__device__ void refine_lds(int L, uint32_t need, int32_t* out, SM& sm) {
+  constexpr int PER = (SM::kCap + NT - 1) / NT;
   for (;; ++L) {
     const Level lv = level_of(L);
     const int nbins = 1 << lv.width;
@@ -154,33 +193,71 @@ __device__ void refine_lds(int L, uint32_t need, int32_t* out, SelSmem& sm) {
     const bool last = (cnt == need - above);
     if (threadIdx.x == 0) sm.ntie = 0;
     __syncthreads();
+    // Emit and keep with one LDS atomic per wave for each, over all PER elements.
+    uint64_t me[PER], mk[PER];
+    int te = 0, tk = 0;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
       const int t = (int)threadIdx.x + e * NT;
       uint32_t d = 0;
       if (t < nt) d = (uint32_t)(composite_key(k_[e], i_[e]) >> lv.shift) & dmask;
-      const bool emit = (t < nt) && (d > b || (last && d == b));
-      const bool keep = (t < nt) && !last && d == b;
-      const int so = wave_append_slot(emit, &sm.nout);
-      if (emit) out[so] = i_[e];
-      const int sk = wave_append_slot(keep, &sm.ntie);
-      if (keep) {
+      me[e] = wave_ballot((t < nt) && (d > b || (last && d == b)));
+      mk[e] = wave_ballot((t < nt) && !last && d == b);
+      te += __builtin_popcountll(me[e]);
+      tk += __builtin_popcountll(mk[e]);
+    }
+    const int l = lane_id();
+    int be = 0, bk = 0;
+    if (l == 0) {
+      if (te) be = atomicAdd(&sm.nout, te);
+      if (tk) bk = atomicAdd(&sm.ntie, tk);
+    }
+    be = readlane(be, 0);
+    bk = readlane(bk, 0);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      if ((me[e] >> l) & 1) out[be + mask_prefix(me[e])] = i_[e];
+      if ((mk[e] >> l) & 1) {
+        const int sk = bk + mask_prefix(mk[e]);
         sm.tkey[sk] = k_[e];
         sm.tidx[sk] = i_[e];
       }
+      be += __builtin_popcountll(me[e]);
+      bk += __builtin_popcountll(mk[e]);
     }
     __syncthreads();
     if (last) return;
     need -= above;
+    if (cnt <= (uint32_t)kWave) {
+      // The boundary bin (now the whole tie buffer) fits one wave: wave 0 ranks its
+      // elements by composite key directly instead of running further levels.
+      if (threadIdx.x < kWave) {
+        const bool have = l < (int)cnt;
+        const uint32_t kk = have ? sm.tkey[l] : 0u;
+        const int32_t ix = have ? sm.tidx[l] : 0;
+        const uint64_t K = composite_key(kk, ix);
+        int rank = 0;
+        for (int u = 0; u < (int)cnt; ++u) {
+          const uint64_t Ku = composite_key((uint32_t)readlane((int)kk, u), readlane(ix, u));
+          rank += Ku > K ? 1 : 0;
+        }
+        const bool take = have && rank < (int)need;
+        const uint64_t mt = wave_ballot(take);
+        const int base = sm.nout;
+        if (take) out[base + mask_prefix(mt)] = ix;
+      }
+      __syncthreads();
+      return;
+    }
   }
 }
 
 // Rescan mode: resolve the remaining levels by passes over the whole input.  On entry
 // the digits of levels < L are fixed to `prefix` (the value of K >> (shift of level L-1)),
 // and `need` elements remain to be chosen among those matching it.  Contains barriers.
-template <int NT, class Src>
+template <int NT, class Src, class SM>
 __device__ void refine_rescan(const Src& src, int n, int L, uint64_t prefix, uint32_t need, int32_t* out,
-                              SelSmem& sm) {
+                              SM& sm) {
   int above_shift = level_of(L - 1).shift;
   for (;; ++L) {
     const Level lv = level_of(L);
@@ -212,8 +289,8 @@ __device__ void refine_rescan(const Src& src, int n, int L, uint64_t prefix, uin
 }
 
 // Histogram of the level-1 digit over n elements into sm.hist (sm.hist must be zero).
-template <int NT, class Src>
-__device__ __forceinline__ void hist_level1(const Src& src, int n, SelSmem& sm) {
+template <int NT, class Src, class SM>
+__device__ __forceinline__ void hist_level1(const Src& src, int n, SM& sm) {
   constexpr int U = 4;
   int base = 0;
   for (; base + U * NT <= n; base += U * NT) {
@@ -231,8 +308,8 @@ __device__ __forceinline__ void hist_level1(const Src& src, int n, SelSmem& sm) 
 
 // Top-m of n elements (1 <= m <= n) by composite key; writes exactly m indices to
 // out[0..m) in unspecified order.  All NT threads must call it.  Contains barriers.
-template <int NT, class Src>
-__device__ void block_select(const Src& src, int n, int m, int32_t* out, SelSmem& sm) {
+template <int NT, class Src, class SM>
+__device__ void block_select(const Src& src, int n, int m, int32_t* out, SM& sm) {
   if (threadIdx.x == 0) {
     sm.nout = 0;
     sm.ntie = 0;
@@ -258,7 +335,7 @@ __device__ void block_select(const Src& src, int n, int m, int32_t* out, SelSmem
     __syncthreads();
     return;
   }
-  if (cnt <= (uint32_t)kTieCap) {
+  if (cnt <= (uint32_t)SM::kCap) {
     for (int base = 0; base < n; base += NT) {
       const int j = base + (int)threadIdx.x;
       uint32_t k = 0;
@@ -288,15 +365,17 @@ __device__ void block_select(const Src& src, int n, int m, int32_t* out, SelSmem
 }
 
 // m-th largest order key of n elements (1 <= m <= n): three value levels, each a pass
-// over the input.  Returns the key in every thread.  Contains barriers.
-template <int NT, class Src>
-__device__ uint32_t block_kth_key(const Src& src, int n, int m, SelSmem& sm) {
+// over the input.  Returns the key in every thread; with fewer levels, the smallest key of
+// the m-th key's bin at the last level (a lower bound of the m-th key).  Contains barriers.
+template <int NT, class Src, class SM, int LEVELS = 3>
+__device__ uint32_t block_kth_key(const Src& src, int n, int m, SM& sm) {
   uint32_t prefix = 0;
   int above_shift = 32;
   uint32_t need = (uint32_t)m;
-  const int shifts[3] = {20, 8, 0};
-  const int widths[3] = {12, 12, 8};
-  for (int L = 0; L < 3; ++L) {
+  constexpr int shifts[3] = {20, 8, 0};
+  constexpr int widths[3] = {12, 12, 8};
+#pragma unroll
+  for (int L = 0; L < LEVELS; ++L) {
     const int sh = shifts[L];
     const int nbins = 1 << widths[L];
     zero_hist<NT>(sm, nbins);
@@ -317,7 +396,151 @@ __device__ uint32_t block_kth_key(const Src& src, int n, int m, SelSmem& sm) {
     prefix = (prefix << widths[L]) | b;
     above_shift = sh;
   }
-  return prefix;
+  return prefix << shifts[LEVELS - 1];  // LEVELS < 3: the lower edge of the m-th key's bin
+}
+
+// Top-m of a materialised row x[0..n) (1 <= m < n) with one full pass over it:
+//   1. rows longer than the candidate buffer take a sample of kSelSamples order keys in
+//      NSEG evenly spaced runs of consecutive elements (a few per cent of the row) and a
+//      threshold T = the lower edge of the 12-bit bin of the sample's r-th largest key
+//      (keys normalised over the sample's range), r = ceil(1.75 m samples / n), so that
+//      about 1.75 m elements of the row are expected at or above T, well inside [m, kCap]
+//      (shorter rows: T = 0, every element);
+//   2. one pass appends every element with key >= T to the LDS buffer (counting past its
+//      capacity), with 16-byte loads issued one step ahead when the row is 16-byte
+//      aligned, and one LDS atomic per wave and step;
+//   3. if the buffer holds between m and SM::kCap elements, its keys are normalised over
+//      [T, max] and the radix levels 1.. refine it in LDS; otherwise block_select() reruns
+//      the row exactly with full passes.
+// The result is exact either way; the sample only decides how much work is done.
+constexpr int kSelSamples = 2048;
+
+template <int NT, class SM>
+__device__ void block_select_sampled(const float* x, int n, int m, int32_t* out, SM& sm) {
+  static_assert(SM::kCap >= kSelSamples, "the sample lives in the candidate buffer");
+  constexpr int SEG = 64, NSEG = kSelSamples / SEG;  // 32 runs of 64 consecutive keys
+  const int l = lane_id();
+  uint32_t T = 0;
+  if (threadIdx.x == 0) {
+    sm.kmin = 0xFFFFFFFFu;
+    sm.kmax = 0u;
+  }
+  __syncthreads();
+  if (n > SM::kCap) {
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    for (int t = threadIdx.x; t < kSelSamples; t += NT) {
+      const int seg = t / SEG, e = t % SEG;
+      const int64_t start = (int64_t)seg * (n - SEG) / (NSEG - 1);
+      const uint32_t k = order_key(x[start + e]);
+      sm.tkey[t] = k;
+      lo = min(lo, k);
+      hi = max(hi, k);
+    }
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
+    if (l == 0) {
+      atomicMin(&sm.kmin, lo);
+      atomicMax(&sm.kmax, hi);
+    }
+    __syncthreads();
+    const KeyNorm nz = key_norm(sm.kmin, sm.kmax);
+    for (int t = threadIdx.x; t < kSelSamples; t += NT) sm.tkey[t] = nz.normalize(sm.tkey[t]);
+    __syncthreads();
+    int64_t rank = ((int64_t)7 * m * kSelSamples + (int64_t)4 * n - 1) / ((int64_t)4 * n);  // ceil(1.75 m S / n)
+    rank = rank < 1 ? 1 : (rank > kSelSamples ? kSelSamples : rank);
+    T = nz.denormalize(block_kth_key<NT, LdsKeySrc, SM, 1>(LdsKeySrc{sm.tkey}, kSelSamples, (int)rank, sm));
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    sm.ntie = 0;
+    sm.nout = 0;
+    sm.kmax = 0u;
+  }
+  __syncthreads();
+  uint32_t kmax = 0u;
+  // Appends the lanes' keys k_[u] (element j0 + u * ustride) that pass, one LDS atomic per wave.
+  auto append = [&](const uint32_t* k_, const bool* ok, int j0, int ustride, auto Uc) __attribute__((always_inline)) {
+    constexpr int U = decltype(Uc)::value;
+    uint64_t mk[U];
+    int tot = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      mk[u] = wave_ballot(ok[u] && k_[u] >= T);
+      tot += __builtin_popcountll(mk[u]);
+    }
+    if (tot) {  // wave-uniform
+      int at = 0;
+      if (l == 0) at = atomicAdd(&sm.ntie, tot);
+      at = readlane(at, 0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if ((mk[u] >> l) & 1) {
+          const int slot = at + mask_prefix(mk[u]);
+          if (slot < SM::kCap) {
+            sm.tkey[slot] = k_[u];
+            sm.tidx[slot] = j0 + u * ustride;
+          }
+          kmax = max(kmax, k_[u]);
+        }
+        at += __builtin_popcountll(mk[u]);
+      }
+    }
+  };
+  int done = 0;  // elements [0, done) handled by the vector loop
+  if ((reinterpret_cast<uintptr_t>(x) & 15) == 0) {
+    // 16-byte loads, UV per thread per step, the next step's loads issued before this
+    // step's keys are tested.
+    constexpr int UV = 4;
+    const float4* xv = reinterpret_cast<const float4*>(x);
+    const int nv = n / 4;
+    float4 cur[UV], nxt[UV];
+    auto load = [&](float4* v, int base) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < UV; ++u) {
+        const int jv = base + u * NT + (int)threadIdx.x;
+        v[u] = jv < nv ? xv[jv] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    };
+    if (nv > 0) load(cur, 0);
+    for (int base = 0; base < nv; base += UV * NT) {
+      if (base + UV * NT < nv) load(nxt, base + UV * NT);
+#pragma unroll
+      for (int u = 0; u < UV; ++u) {
+        const int jv = base + u * NT + (int)threadIdx.x;
+        const uint32_t k_[4] = {order_key(cur[u].x), order_key(cur[u].y), order_key(cur[u].z), order_key(cur[u].w)};
+        const bool ok[4] = {jv < nv, jv < nv, jv < nv, jv < nv};
+        append(k_, ok, 4 * jv, 1, std::integral_constant<int, 4>{});
+      }
+#pragma unroll
+      for (int u = 0; u < UV; ++u) cur[u] = nxt[u];
+    }
+    done = nv * 4;
+  }
+  constexpr int U = 8;
+  for (int base = done; base < n; base += U * NT) {
+    uint32_t k_[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = base + u * NT + (int)threadIdx.x;
+      ok[u] = j < n;
+      k_[u] = ok[u] ? order_key(x[j]) : 0u;
+    }
+    append(k_, ok, base + (int)threadIdx.x, NT, std::integral_constant<int, U>{});
+  }
+  kmax = wave_max_u32(kmax);
+  if (l == 0 && kmax) atomicMax(&sm.kmax, kmax);
+  __syncthreads();
+  const int c = sm.ntie;
+  const KeyNorm nz = key_norm(T, sm.kmax);
+  __syncthreads();
+  if (c >= m && c <= SM::kCap) {
+    for (int t = threadIdx.x; t < c; t += NT) sm.tkey[t] = nz.normalize(sm.tkey[t]);
+    __syncthreads();
+    refine_lds<NT>(1, (uint32_t)m, out, sm);
+  } else {
+    block_select<NT>(RowSrc{x}, n, m, out, sm);
+  }
 }
 
 }  // namespace idx

@@ -191,6 +191,32 @@ def test_select_all_equal_rows_force_rescan():
         assert_same_sets(got, ref, f"split={split}")
 
 
+def _sample_positions(n, seg=64, nseg=64):
+    """Positions the single-workgroup select samples (runs of 64 at evenly spaced starts)."""
+    starts = [i * (n - seg) // (nseg - 1) for i in range(nseg)]
+    return np.concatenate([np.arange(a, a + seg) for a in starts])
+
+
+def test_select_sampled_threshold_misjudged():
+    """Rows built so the sampled threshold misjudges them: too few candidates (the sample
+    holds the only large values), too many (the sample holds the only small ones), a
+    sample that lands exactly on the k-th value, and a short row below the buffer size.
+    Every case must still equal the oracle (the exact fallback takes over)."""
+    rng = np.random.default_rng(21)
+    ld, k = 65536, 2048
+    x = rng.uniform(0.0, 0.5, size=(5, ld)).astype(np.float32)
+    pos = _sample_positions(ld)
+    x[0, pos[:300]] = 1.0 + rng.uniform(0, 1e-3, size=300).astype(np.float32)   # count(>= T) < k
+    x[1] += 1.0                                                                  # count(>= T) > buffer
+    x[1, pos] = rng.uniform(0.0, 0.5, size=len(pos)).astype(np.float32)
+    x[2, :] = np.float32(0.25)                                                   # all equal: rescan
+    x[3, pos] = np.float32(0.75)                                                 # 4096 equal sample values
+    n = np.array([ld, ld, ld, ld, 6000], dtype=np.int32)
+    ref = oracle.select_rows(x, n, k)
+    got = sai.idx_select(torch.from_numpy(x).cuda(), torch.from_numpy(n).cuda(), k, split=0).cpu().numpy()
+    assert_same_sets(got, ref, "sampled select")
+
+
 def test_select_short_and_empty_rows():
     rng = np.random.default_rng(3)
     x = rng.standard_normal((5, 300)).astype(np.float32)
