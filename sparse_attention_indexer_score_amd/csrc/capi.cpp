@@ -287,6 +287,7 @@ int idx_fused_topk(const idx_problem* p, int32_t k, int32_t* out_idx, void* ws, 
   F.thr = reinterpret_cast<float*>(base + z.off_thr);
   F.cnt = reinterpret_cast<int32_t*>(base + z.off_cnt);
   F.stats = reinterpret_cast<long long*>(base + z.off_stats);
+  F.want_stats = stats != nullptr;
   F.fb_ctrl = reinterpret_cast<int32_t*>(base + z.off_fb);
   F.fb_list = F.fb_ctrl + 2;
   F.slab_s = reinterpret_cast<float*>(base + z.off_slab_s);

@@ -821,7 +821,7 @@ struct ThrArgs {
 };
 
 __global__ __launch_bounds__(kThreads) void threshold_kernel(ThrArgs T) {
-  __shared__ SelSmem sm;
+  __shared__ SelSmemT<64> sm;  // histogram and scan scratch only
   const int r = blockIdx.x;
   if (r == 0 && threadIdx.x < kStatSlots) T.stats[threadIdx.x] = (threadIdx.x == kStatMin) ? 0x7FFFFFFF : 0;
   if (r == 0 && threadIdx.x < 2) T.fb_ctrl[threadIdx.x] = 0;
@@ -842,12 +842,53 @@ __global__ __launch_bounds__(kThreads) void threshold_kernel(ThrArgs T) {
     if (n <= 0) {
       tr = -__builtin_inff();
     } else {
-      // m-th largest of n samples; m = ceil(2.25 * k * n / V) so that ~2.25k keys pass.
+      // Rank m = ceil(2.25 * k * n / V), so that ~2.25k keys pass.  The threshold is the
+      // lower edge of the m-th largest sample's bin at 24 bits of the sample keys
+      // normalised over [min, max]: a min/max pass, then two 12-bit histogram passes (the
+      // second over the first boundary bin only).  A lower bound of that sample that adds
+      // the keys of one fine bin; the second level keeps the bin fine when a few far
+      // larger samples stretch the range.
       int64_t m = ((int64_t)9 * T.k * n + 4 * (int64_t)V - 1) / (4 * (int64_t)V);
       if (m < 1) m = 1;
       if (m > n) m = n;
-      const uint32_t key = block_kth_key<kThreads>(RowSrc{T.samp + (int64_t)r * T.ns + jlo}, n, (int)m, sm);
-      tr = order_key_to_float(key);
+      const float* sp = T.samp + (int64_t)r * T.ns + jlo;
+      if (threadIdx.x == 0) {
+        sm.kmin = 0xFFFFFFFFu;
+        sm.kmax = 0u;
+      }
+      zero_hist<kThreads>(sm, kHistBins);
+      __syncthreads();
+      uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+      for (int j = threadIdx.x; j < n; j += kThreads) {
+        const uint32_t k = order_key(sp[j]);
+        lo = min(lo, k);
+        hi = max(hi, k);
+      }
+      lo = wave_min_u32(lo);
+      hi = wave_max_u32(hi);
+      if (lane_id() == 0) {
+        atomicMin(&sm.kmin, lo);
+        atomicMax(&sm.kmax, hi);
+      }
+      __syncthreads();
+      const KeyNorm nz = key_norm(sm.kmin, sm.kmax);
+      for (int j = threadIdx.x; j < n; j += kThreads)
+        atomicAdd(&sm.hist[nz.normalize(order_key(sp[j])) >> (32 - kHistBits)], 1u);
+      __syncthreads();
+      find_boundary<kThreads>(sm, kHistBins, (uint32_t)m);
+      const uint32_t b1 = (uint32_t)sm.bnd_bin;
+      const uint32_t m2 = (uint32_t)m - sm.bnd_above;
+      __syncthreads();
+      zero_hist<kThreads>(sm, kHistBins);
+      __syncthreads();
+      for (int j = threadIdx.x; j < n; j += kThreads) {
+        const uint32_t v = nz.normalize(order_key(sp[j]));
+        if ((v >> (32 - kHistBits)) == b1) atomicAdd(&sm.hist[(v >> (32 - 2 * kHistBits)) & (kHistBins - 1)], 1u);
+      }
+      __syncthreads();
+      find_boundary<kThreads>(sm, kHistBins, m2);
+      const uint32_t v = (b1 << (32 - kHistBits)) | ((uint32_t)sm.bnd_bin << (32 - 2 * kHistBits));
+      tr = order_key_to_float(nz.denormalize(v));
     }
   }
   if (threadIdx.x == 0) T.thr[r] = tr;
@@ -865,10 +906,26 @@ struct SlabArgs {
   long long* stats;
   int32_t* fb_ctrl;
   int32_t* fb_list;
-  int32_t k, cap;
+  int32_t k, cap, want_stats;
 };
 
-__global__ __launch_bounds__(kThreads) void slab_select_kernel(SlabArgs S) {
+// Candidates of a slab row with keys normalised over the row's [min, max] candidate key:
+// their raw keys share their top bits, so without this the first 12-bit radix level would
+// put nearly all of them in one bin (and overflow the tie buffer into rescans).
+struct NormPairSrc {
+  const float* s;
+  const int32_t* i;
+  KeyNorm nz;
+  __device__ __forceinline__ uint32_t key(int j) const { return nz.normalize(order_key(s[j])); }
+  __device__ __forceinline__ int32_t index(int j) const { return i[j]; }
+};
+
+// One 512-thread workgroup per row (three per CU): a min/max pass over the row's slab
+// candidates, then block_select() over their normalised keys; the candidates stay in L2
+// across its passes.
+constexpr int kSlabThreads = 512;
+
+__global__ __launch_bounds__(kSlabThreads) void slab_select_kernel(SlabArgs S) {
   __shared__ SelSmem sm;
   const int r = blockIdx.x;
   const int V = S.ke[r] - S.ks[r];
@@ -877,19 +934,40 @@ __global__ __launch_bounds__(kThreads) void slab_select_kernel(SlabArgs S) {
   int32_t* out = S.out + (int64_t)r * S.k;
   const bool bad = c > S.cap || c < need;
   if (threadIdx.x == 0) {
-    atomicAdd((unsigned long long*)&S.stats[V <= S.cap ? kStatStoreAll : kStatSampled], 1ull);
-    atomicMax((unsigned long long*)&S.stats[kStatMax], (unsigned long long)c);
-    if (V > S.cap) atomicMin((unsigned long long*)&S.stats[kStatMin], (unsigned long long)c);
-    atomicAdd((unsigned long long*)&S.stats[kStatTotal], (unsigned long long)c);
+    if (S.want_stats) {  // same-address atomics from every row: only when asked for
+      atomicAdd((unsigned long long*)&S.stats[V <= S.cap ? kStatStoreAll : kStatSampled], 1ull);
+      atomicMax((unsigned long long*)&S.stats[kStatMax], (unsigned long long)c);
+      if (V > S.cap) atomicMin((unsigned long long*)&S.stats[kStatMin], (unsigned long long)c);
+      atomicAdd((unsigned long long*)&S.stats[kStatTotal], (unsigned long long)c);
+    }
     if (bad) {
       atomicAdd((unsigned long long*)&S.stats[kStatFallback], 1ull);
       S.fb_list[atomicAdd(&S.fb_ctrl[0], 1)] = r;
     }
+    sm.kmin = 0xFFFFFFFFu;
+    sm.kmax = 0u;
   }
   if (bad) return;  // uniform: the fallback writes this row
-  if (need > 0)
-    block_select<kThreads>(PairSrc{S.slab_s + (int64_t)r * S.cap, S.slab_i + (int64_t)r * S.cap}, c, need, out, sm);
-  for (int j = need + threadIdx.x; j < S.k; j += kThreads) out[j] = -1;
+  const float* ss = S.slab_s + (int64_t)r * S.cap;
+  const int32_t* si = S.slab_i + (int64_t)r * S.cap;
+  if (need > 0) {
+    __syncthreads();
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    for (int j = threadIdx.x; j < c; j += kSlabThreads) {
+      const uint32_t k = order_key(ss[j]);
+      lo = min(lo, k);
+      hi = max(hi, k);
+    }
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
+    if (lane_id() == 0) {
+      atomicMin(&sm.kmin, lo);
+      atomicMax(&sm.kmax, hi);
+    }
+    __syncthreads();
+    block_select<kSlabThreads>(NormPairSrc{ss, si, key_norm(sm.kmin, sm.kmax)}, c, need, out, sm);
+  }
+  for (int j = need + threadIdx.x; j < S.k; j += kSlabThreads) out[j] = -1;
 }
 
 // ----------------------------------------------------------------------------- K4
@@ -1158,7 +1236,8 @@ hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_id
     S.fb_list = F.fb_list;
     S.k = F.k;
     S.cap = F.cap;
-    slab_select_kernel<<<dim3(P.rows), dim3(kThreads), 0, s>>>(S);
+    S.want_stats = F.want_stats;
+    slab_select_kernel<<<dim3(P.rows), dim3(kSlabThreads), 0, s>>>(S);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(4)) != hipSuccess) return e;
   }

@@ -33,6 +33,7 @@ struct FusedPlan {
   float* thr;
   int32_t* cnt;
   long long* stats;  // kStatSlots
+  int32_t want_stats;  // update the route counters (only when the caller asks for them)
   int32_t* fb_ctrl;  // [0] count, [1] head
   int32_t* fb_list;
   float* slab_s;
