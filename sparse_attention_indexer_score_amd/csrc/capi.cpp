@@ -131,7 +131,7 @@ FusedSizes fused_sizes(const idx_problem* p, int32_t k) {
   z.off_scratch = o;
   o = round_up(o + (size_t)z.fb_blocks * (size_t)z.scratch_ld * 4, kAlign);
   z.off_lin = o;
-  o = round_up(o + (paged ? 0 : lin_ws_bytes((int32_t)rows)), kAlign);
+  o = round_up(o + lin_ws_bytes((int32_t)rows), kAlign);
   z.total = o;
   return z;
 }
@@ -228,7 +228,7 @@ int idx_select(const float* scores, int64_t ld, const int32_t* row_start, const 
 
 size_t idx_score_workspace(const idx_problem* p) {
   if (check_problem(p, nullptr) != IDX_OK) return 0;
-  if (p->page_table || p->rows == 0) return 0;
+  if (p->rows == 0) return 0;
   return lin_ws_bytes(p->rows);
 }
 
@@ -295,7 +295,7 @@ int idx_fused_topk(const idx_problem* p, int32_t k, int32_t* out_idx, void* ws, 
   F.samp = reinterpret_cast<float*>(base + z.off_samp);
   F.scratch = reinterpret_cast<float*>(base + z.off_scratch);
   F.lin_q8 = F.lin_sf = nullptr;
-  if (!p->page_table) lin_carve(base + z.off_lin, p->rows, &F.lin_q8, &F.lin_sf);
+  lin_carve(base + z.off_lin, p->rows, &F.lin_q8, &F.lin_sf);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((rc = hip_err(launch_fused(P, F, out_idx, s, next_timing_slot())))) return rc;
   if (stats) {

@@ -30,9 +30,9 @@ constexpr int kThreads = 256;  // 4 waves per workgroup
 constexpr int kTile = 32;      // keys per MFMA block
 
 // Rows per workgroup: 4 waves x RowsPerWave (contiguous kernel: 4 rows per wave for MXFP4
-// at 32 heads, else 2); the paged kernel holds 4 rows per wave at 32 heads.
+// at 32 heads, else 2); the paged kernel holds one row pair in all four waves.
 int rows_per_block(int heads, int fmt) { return 4 * (heads == 32 && fmt == FMT_MXFP4 ? 4 : 2); }
-static int rows_per_block_paged(int heads) { return 4 * (heads == 64 ? 2 : 4); }
+static int rows_per_block_paged(int) { return 2; }  // score_pages_kernel: one row pair
 static int rows_per_block_for(const DevProblem& P) {
   return P.page_table ? rows_per_block_paged(P.heads) : rows_per_block(P.heads, P.fmt);
 }
@@ -99,128 +99,6 @@ __device__ __forceinline__ int64_t map_item(const TileWork& W) {
   const int64_t x = b & 7, local = b >> 3;
   const int64_t g = local / W.nrb, j = local % W.nrb;
   return (g * 8 + x) * W.nrb + j;
-}
-
-__device__ __forceinline__ float finish_score(float head_sum, float kscale) { return head_sum * kscale; }
-
-template <int FMT, int H, int MODE, bool PAGED>
-__global__ __launch_bounds__(kThreads) void score_kernel(ScoreArgs A, EpiArgs E, TileWork W) {
-  constexpr int RW = (H == 64) ? 2 : 4;  // rows per wave
-  constexpr int RB = 4 * RW;             // rows per workgroup
-  const int64_t item = map_item(W);
-  if (item >= W.total) return;
-  const int rb = (int)(item % W.nrb);
-  const int chunk = (int)(item / W.nrb);
-  const int wave = threadIdx.x / kWave;
-  const int l = lane_id();
-  const int row0 = rb * RB + wave * RW;
-  const int phase = (MODE == MODE_SAMPLE) ? sample_phase(rb, E.stride) : 0;
-
-  // Positions are keys (STORE/FILTER) or sample slots (SAMPLE); plo/phi: valid range.
-  int plo[RW], phi[RW], ksr[RW];
-  float thr[RW];
-  int wlo = 0x7FFFFFFF, whi = 0;
-#pragma unroll
-  for (int i = 0; i < RW; ++i) {
-    const int r = row0 + i;
-    plo[i] = 0;
-    phi[i] = 0;
-    ksr[i] = 0;
-    thr[i] = 0.0f;
-    if (r < A.rows) {
-      const int ks = A.ks[r], ke = A.ke[r];
-      ksr[i] = ks;
-      if (MODE == MODE_SAMPLE) {
-        if (ke - ks > E.skip_le) sample_range(ks, ke, phase, E.stride, plo[i], phi[i]);
-      } else {
-        plo[i] = ks;
-        phi[i] = ke;
-      }
-      if (MODE == MODE_FILTER) thr[i] = E.thr[r];
-      if (phi[i] > plo[i]) {
-        wlo = min(wlo, plo[i]);
-        whi = max(whi, phi[i]);
-      }
-    }
-  }
-  const int c0 = chunk * W.chunk, c1 = c0 + W.chunk;
-  const int t0 = max(c0, wlo) / kTile, t1 = (min(c1, whi) + kTile - 1) / kTile;
-  if (t0 >= t1) return;  // wave-uniform: nothing visible in this chunk
-
-  RowOperand<FMT, H> ro[RW];
-#pragma unroll
-  for (int i = 0; i < RW; ++i)
-    if (row0 + i < A.rows) load_row<FMT, H>(ro[i], A, row0 + i);
-
-  for (int t = t0; t < t1; ++t) {
-    const int pos = t * kTile + (l & 31);
-    const int64_t key = (MODE == MODE_SAMPLE) ? (int64_t)phase + (int64_t)pos * E.stride : (int64_t)pos;
-    KeyOperand kshared;
-    int64_t phys_shared = 0;
-    if constexpr (!PAGED) {
-      phys_shared = key < A.num_keys ? key : 0;
-      load_key_global<FMT>(kshared, A, phys_shared);
-    }
-#pragma unroll
-    for (int i = 0; i < RW; i += 2) {
-      const bool actA = plo[i] < (t + 1) * kTile && phi[i] > t * kTile;
-      const bool actB = plo[i + 1] < (t + 1) * kTile && phi[i + 1] > t * kTile;
-      if (!actA && !actB) continue;
-      float pa = 0.0f, pb = 0.0f;
-      int64_t physA = phys_shared, physB = phys_shared;
-      if constexpr (PAGED) {
-        const bool vA = pos >= plo[i] && pos < phi[i];
-        const bool vB = pos >= plo[i + 1] && pos < phi[i + 1];
-        physA = vA ? physical_key(A, row0 + i, key) : 0;
-        physB = vB ? physical_key(A, row0 + i + 1, key) : 0;
-        if (actA) {
-          KeyOperand ko;
-          load_key_global<FMT>(ko, A, physA);
-          pa = row_partial<FMT, H>(ro[i], ko);
-        }
-        if (actB) {
-          KeyOperand ko;
-          load_key_global<FMT>(ko, A, physB);
-          pb = row_partial<FMT, H>(ro[i + 1], ko);
-        }
-      } else {
-        if (actA) pa = row_partial<FMT, H>(ro[i], kshared);
-        if (actB) pb = row_partial<FMT, H>(ro[i + 1], kshared);
-      }
-      const float hs = combine_halves(pa, pb);
-      const bool upper = l >= 32;
-      const int ri = upper ? i + 1 : i;
-      const int r = row0 + ri;
-      const int64_t phys = upper ? physB : physA;
-      const bool valid = pos >= (upper ? plo[i + 1] : plo[i]) && pos < (upper ? phi[i + 1] : phi[i]);
-      const float score = finish_score(hs, key_scale(A, valid ? phys : 0));
-      const int ks = upper ? ksr[i + 1] : ksr[i];
-      if constexpr (MODE == MODE_STORE) {
-        if (valid) E.out[(int64_t)r * E.ld + (key - ks)] = score;
-      } else if constexpr (MODE == MODE_SAMPLE) {
-        if (valid) E.samp[(int64_t)r * E.ns + pos] = score;
-      } else {
-        const float tr = upper ? thr[i + 1] : thr[i];
-        const bool pred = valid && score >= tr;
-        const uint64_t m = wave_ballot(pred);
-        if (m) {
-          const uint32_t mA = (uint32_t)m, mB = (uint32_t)(m >> 32);
-          int baseA = 0, baseB = 0;
-          if (l == 0 && mA) baseA = atomicAdd(&E.cnt[row0 + i], __builtin_popcount(mA));
-          if (l == 32 && mB) baseB = atomicAdd(&E.cnt[row0 + i + 1], __builtin_popcount(mB));
-          baseA = readlane(baseA, 0);
-          baseB = readlane(baseB, 32);
-          const int before = mask_prefix(m) - (upper ? __builtin_popcount(mA) : 0);
-          const int slot = (upper ? baseB : baseA) + before;
-          if (pred && slot < E.cap) {
-            const int64_t o = (int64_t)r * E.cap + slot;
-            E.slab_s[o] = score;
-            E.slab_i[o] = (int32_t)(key - ks);
-          }
-        }
-      }
-    }
-  }
 }
 
 // ============================================================================= contiguous K
@@ -466,21 +344,22 @@ struct StageLds {
   int32_t* cand_i; //         and their key indices relative to ks
 };
 
-// FILTER mode: each wave collects the candidates of its own rows in LDS (no atomics: the
-// rows are the wave's alone) and moves them to the global slab in batches, with one
-// global atomic per row and batch instead of one per tile.
+// FILTER mode: each wave collects its candidates in an LDS buffer of its own (no LDS
+// atomics) and moves them to the global slab in batches, with one global atomic per row
+// and batch instead of one per tile (waves that share rows flush separately).
 constexpr int kCandBuf = 256;
 
 // Scores of the RW rows [row0, row0 + RW) of this wave on the workgroup's tiles [tA, tB)
 // (positions: keys, or sample slots with key = phase + pos * S), with the epilogue of MODE.
-// Every wave of the workgroup must call it with the same tA, tB.  MAIN mode: every wave
-// scores every tile that meets its rows.  FALLBACK mode: all waves hold the same rows and
-// wave w scores tiles w and w + 4 of each stage; MODE_ROWSTORE then writes only row E.only_row, to
-// E.out[key - ks].
-template <int FMT, int H, int MODE, int RW, bool FALLBACK>
+// Every wave of the workgroup must call it with the same tA, tB.  Default: every wave has
+// rows of its own and scores every tile that meets them.  SHARED: all waves hold the same
+// rows and wave w scores tiles w and w + 4 of each stage (paged keys, the fallback).
+// rmask selects the rows that count (the others see no keys); req >= 0 reads keys through
+// request req's page table.  MODE_ROWSTORE writes only row E.only_row, to E.out[key - ks].
+template <int FMT, int H, int MODE, int RW, bool SHARED>
 __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, const EpiArgs& E, int row0,
                                          int phase, int S, int c0, int c1, int tA, int tB,
-                                         const StageLds<FMT>& sl) {
+                                         const StageLds<FMT>& sl, int req = -1, uint32_t rmask = ~0u) {
   static_assert(RW % 2 == 0, "rows are processed in pairs");
   using G = StageGeom<FMT>;
   constexpr int KB = G::kKB;
@@ -491,12 +370,14 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
 
   int plo[RW], phi[RW], ksr[RW];
   int wlo = 0x7FFFFFFF, whi = 0, full_lo = 0, full_hi = 0x7FFFFFFF;
+  int lmax = 0;  // paged: largest logical key any active row sees
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
     const int r = row0 + i;
     plo[i] = phi[i] = ksr[i] = 0;
-    if (r < A.rows) {
+    if (r < A.rows && ((rmask >> i) & 1)) {
       const int ks = uniform(A.ks[r]), ke = uniform(A.ke[r]);
+      lmax = max(lmax, ke - 1);
       ksr[i] = ks;
       if (MODE == MODE_SAMPLE) {
         if (ke - ks > E.skip_le) sample_range(ks, ke, phase, S, plo[i], phi[i]);
@@ -535,9 +416,14 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
     if (MODE == MODE_FILTER && row0 + i < A.rows) thr_l[p] = E.thr[row0 + i];
   }
   const int64_t last_key = A.num_keys - 1;
+  // Physical key of stage position pos: contiguous keys are clamped to the key array;
+  // paged keys (all rows of request `req`) are clamped to the rows' visible range, then
+  // mapped through the request's page table (64 keys per page).
   auto key_of = [&](int64_t pos) -> int64_t {
     const int64_t key = (int64_t)phase + pos * S;
-    return key < last_key ? key : last_key;
+    if (req < 0) return key < last_key ? key : last_key;
+    const int64_t lk = key < lmax ? key : lmax;
+    return (int64_t)A.page_table[(int64_t)req * A.max_pages + (lk >> 6)] * kPage + (lk & (kPage - 1));
   };
 
   // FILTER: this wave's LDS candidate buffers and their (wave-uniform) fill counts.
@@ -741,7 +627,7 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
     for (int i = 0; i < G::kTiles; ++i) {
       const int t = tbase + i;
       if (t >= tB) break;  // workgroup-uniform
-      const bool mine = FALLBACK ? ((i & 3) == wave) : (t >= wt0 && t < wt1);
+      const bool mine = SHARED ? ((i & 3) == wave) : (t >= wt0 && t < wt1);
       if (mine) compute(buf, i, t);
     }
     if (more) lwrite(buf ^ 1);
@@ -804,6 +690,48 @@ __global__ __launch_bounds__(kThreads, 2) void score_tiles_kernel(ScoreArgs A, L
   if (tA >= tB) return;  // workgroup-uniform
   const StageLds<FMT> sl{sh.codes, sh.sf, sh.ks, cand.s, cand.i};
   wg_tiles<FMT, H, MODE, RW, false>(A, L, E, rb * 4 * RW + wave * RW, phase, S, c0, c1, tA, tB, sl);
+}
+
+// Paged keys: one workgroup per (row pair, key chunk).  The pair's rows must read the same
+// request's pages to share the LDS stage, so a pair that straddles two requests is scored
+// in two passes, one row each.  All four waves hold the pair and split each stage's tiles.
+template <int FMT, int H, int MODE>
+__global__ __launch_bounds__(kThreads, 2) void score_pages_kernel(ScoreArgs A, LinArgs L, EpiArgs E, TileWork W) {
+  __shared__ StageShared<FMT> sh;
+  __shared__ CandShared<2, MODE == MODE_FILTER> cand;
+  const int64_t item = map_item(W);
+  if (item >= W.total) return;
+  const int pr = (int)(item % W.nrb);
+  const int chunk = (int)(item / W.nrb);
+  const int row0 = 2 * pr;
+  const int S = (MODE == MODE_SAMPLE) ? E.stride : 1;
+  const int phase = (MODE == MODE_SAMPLE) ? sample_phase(pr, S) : 0;
+  const int c0 = chunk * W.chunk, c1 = c0 + W.chunk;
+  const bool two = row0 + 1 < A.rows;
+  const int q0 = A.row_req[row0], q1 = two ? A.row_req[row0 + 1] : q0;
+  const StageLds<FMT> sl{sh.codes, sh.sf, sh.ks, cand.s, cand.i};
+  for (int pass = 0; pass < (q0 == q1 ? 1 : 2); ++pass) {  // workgroup-uniform
+    const uint32_t rmask = q0 == q1 ? 3u : (1u << pass);
+    const int req = pass == 0 ? q0 : q1;
+    int lo = 0x7FFFFFFF, hi = 0;
+    for (int i = 0; i < 2; ++i) {
+      const int r = row0 + i;
+      if (r >= A.rows || !((rmask >> i) & 1)) continue;
+      const int ks = A.ks[r], ke = A.ke[r];
+      int plo = ks, phi = ke;
+      if (MODE == MODE_SAMPLE) {
+        plo = phi = 0;
+        if (ke - ks > E.skip_le) sample_range(ks, ke, phase, S, plo, phi);
+      }
+      if (phi > plo) {
+        lo = min(lo, plo);
+        hi = max(hi, phi);
+      }
+    }
+    const int tA = max(c0, lo) / kTile, tB = (min(c1, hi) + kTile - 1) / kTile;
+    if (tA < tB) wg_tiles<FMT, H, MODE, 2, true>(A, L, E, row0, phase, S, c0, c1, tA, tB, sl, req, rmask);
+    __syncthreads();
+  }
 }
 
 // ----------------------------------------------------------------------------- K1b
@@ -981,49 +909,10 @@ struct FbArgs {
   int32_t k;
 };
 
-// Paged keys: the row is re-scored with score_kernel's core (row_partial).
-template <int FMT, int H>
-__global__ __launch_bounds__(kThreads) void fallback_paged_kernel(ScoreArgs A, FbArgs F) {
-  __shared__ SelSmem sm;
-  __shared__ int sh_item;
-  const int wave = threadIdx.x / kWave;
-  const int l = lane_id();
-  float* mine = F.scratch + (int64_t)blockIdx.x * F.scratch_ld;
-  for (;;) {
-    if (threadIdx.x == 0) sh_item = atomicAdd(&F.fb_ctrl[1], 1);
-    __syncthreads();
-    const int item = sh_item;
-    __syncthreads();
-    if (item >= F.fb_ctrl[0]) break;  // every wave sees the same item and count
-    const int r = F.fb_list[item];
-    const int ks = A.ks[r], ke = A.ke[r];
-    const int V = ke - ks;
-    RowOperand<FMT, H> ro;
-    load_row<FMT, H>(ro, A, r);
-    // Same 32-key tiles (absolute positions) and lane placement as score_kernel.
-    for (int t = ks / kTile + wave; t * kTile < ke; t += 4) {
-      const int pos = t * kTile + (l & 31);
-      const bool valid = pos >= ks && pos < ke;
-      const int64_t phys = valid ? physical_key(A, r, pos) : 0;
-      KeyOperand ko;
-      load_key_global<FMT>(ko, A, phys);
-      const float p = row_partial<FMT, H>(ro, ko);
-      const float hs = combine_halves(p, p);
-      const float score = finish_score(hs, key_scale(A, phys));
-      if (l < 32 && valid) mine[pos - ks] = score;
-    }
-    __syncthreads();
-    const int need = min(F.k, V);
-    int32_t* out = F.out + (int64_t)r * F.k;
-    if (need > 0) block_select<kThreads>(RowSrc{mine}, V, need, out, sm);
-    for (int j = need + threadIdx.x; j < F.k; j += kThreads) out[j] = -1;
-    __syncthreads();
-  }
-}
 
 
-// Contiguous keys: the row is re-scored by wg_tiles() with the same tiles and lane positions
-// as in score_tiles_kernel (each wave takes two tiles of every stage).  A row's score does
+// The row is re-scored by wg_tiles() with the same per-key arithmetic as the score kernels
+// (contiguous or paged keys; here each wave takes two tiles of every stage).  A row's score does
 // not depend on which rows share its wave: its MFMA outputs, its head reduce, the half-wave
 // sum (low half + high half) and its linear-tile pieces are computed the same way for any
 // pairing, so the scores are bitwise the ones the slab was filtered with.  Only the row
@@ -1049,8 +938,9 @@ __global__ __launch_bounds__(kThreads) void fallback_tiles_kernel(ScoreArgs A, L
       EpiArgs E = {};
       E.out = mine;
       E.only_row = r;
+      const int req = A.page_table ? A.row_req[r] : -1;
       wg_tiles<FMT, H, MODE_ROWSTORE, RW, true>(A, L, E, (r / RW) * RW, 0, 1, ks, ke, ks / kTile,
-                                                (ke + kTile - 1) / kTile, sl);
+                                                (ke + kTile - 1) / kTile, sl, req, 1u << (r % RW));
     }
     __syncthreads();
     const int need = min(F.k, V);
@@ -1120,8 +1010,8 @@ static hipError_t dispatch_score(const DevProblem& P, const LinArgs& L, const Ep
   const ScoreArgs A = score_args(P);
   const dim3 grid = tile_grid(W), block(kThreads);
   if (P.page_table) {  // paged keys are e4m3 (checked at the boundary)
-    if (P.heads == 64) score_kernel<FMT_E4M3, 64, MODE, true><<<grid, block, 0, s>>>(A, E, W);
-    else score_kernel<FMT_E4M3, 32, MODE, true><<<grid, block, 0, s>>>(A, E, W);
+    if (P.heads == 64) score_pages_kernel<FMT_E4M3, 64, MODE><<<grid, block, 0, s>>>(A, L, E, W);
+    else score_pages_kernel<FMT_E4M3, 32, MODE><<<grid, block, 0, s>>>(A, L, E, W);
   } else if (P.fmt == FMT_E4M3) {
     if (P.heads == 64) score_tiles_kernel<FMT_E4M3, 64, MODE><<<grid, block, 0, s>>>(A, L, E, W);
     else score_tiles_kernel<FMT_E4M3, 32, MODE><<<grid, block, 0, s>>>(A, L, E, W);
@@ -1141,7 +1031,7 @@ static int chunk_keys(const DevProblem& P) {
   c = (c + 4095) / 4096 * 4096;
   return (int)std::min<int64_t>(std::max<int64_t>(c, 4096), 16384);
 }
-constexpr int kChunkSamples = 1024;
+constexpr int kChunkSamples = 2048;
 
 size_t lin_ws_bytes(int32_t rows) {
   return (size_t)rows * kLinRowBytes + (((size_t)rows * kLinRowScales + 255) & ~(size_t)255) + 256;
@@ -1155,14 +1045,11 @@ void lin_carve(void* ws, int32_t rows, uint8_t** q8, uint8_t** sf) {
 
 hipError_t launch_score_store(const DevProblem& P, float* out, int64_t ld, void* ws, hipStream_t s) {
   if (P.rows == 0) return hipSuccess;
-  LinArgs L = {nullptr, nullptr};
-  if (!P.page_table) {
-    uint8_t *q8, *sf;
-    lin_carve(ws, P.rows, &q8, &sf);
-    hipError_t e = launch_lin_prep(P, q8, sf, s);
-    if (e != hipSuccess) return e;
-    L = LinArgs{q8, sf};
-  }
+  uint8_t *q8, *sf;
+  lin_carve(ws, P.rows, &q8, &sf);
+  hipError_t e = launch_lin_prep(P, q8, sf, s);
+  if (e != hipSuccess) return e;
+  const LinArgs L{q8, sf};
   EpiArgs E = {};
   E.out = out;
   E.ld = ld;
@@ -1175,7 +1062,7 @@ hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_id
   auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
   if ((e = mark(0)) != hipSuccess) return e;
   const LinArgs L = lin_args(F);
-  if (!P.page_table && (e = launch_lin_prep(P, F.lin_q8, F.lin_sf, s)) != hipSuccess) return e;
+  if ((e = launch_lin_prep(P, F.lin_q8, F.lin_sf, s)) != hipSuccess) return e;
   // K1a: samples
   {
     EpiArgs E = {};
@@ -1252,10 +1139,7 @@ hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_id
     B.out = out_idx;
     B.k = F.k;
     const dim3 grid(F.fb_blocks), block(kThreads);
-    if (P.page_table) {
-      if (P.heads == 64) fallback_paged_kernel<FMT_E4M3, 64><<<grid, block, 0, s>>>(A, B);
-      else fallback_paged_kernel<FMT_E4M3, 32><<<grid, block, 0, s>>>(A, B);
-    } else if (P.fmt == FMT_E4M3) {
+    if (P.fmt == FMT_E4M3) {  // contiguous or paged
       if (P.heads == 64) fallback_tiles_kernel<FMT_E4M3, 64><<<grid, block, 0, s>>>(A, L, B);
       else fallback_tiles_kernel<FMT_E4M3, 32><<<grid, block, 0, s>>>(A, L, B);
     } else {

@@ -1,7 +1,9 @@
-// The indexer scoring core for gfx950, shared by every kernel that produces a score
-// (materialised scores, threshold samples, the fused filter and the exact fallback), so
-// that all of them produce bitwise-identical scores for the same (row, key) — the design
-// rule of the LiteTopK page, section 1 (scoring core identical, only the epilogue differs).
+// The indexer scoring core for gfx950: operand formats, register-resident query operands,
+// key operands and the half-wave combine, shared by every kernel that produces a score
+// (materialised scores, threshold samples, the fused filter and the exact fallback all run
+// one tile routine), so that all of them produce bitwise-identical scores for the same
+// (row, key) — the design rule of the LiteTopK page, section 1 (scoring core identical,
+// only the epilogue differs).
 //
 //   score[r, s] = kscale[s] * sum_h w[r, h] * max(q[r, h] . k[s], 0)
 //
@@ -10,9 +12,8 @@
 // lane l holds head / key (l % 32) and the 32 consecutive head_dim elements
 // [32*(l/32), +32) of the K-step (fp8: 32 bytes, fp4: 16 bytes), with that block's e8m0
 // scale (fixed 127 = 1.0 for e4m3).  The accumulator gives lane l key (l % 32) and heads
-// 8*(i/4) + 4*(l/32) + (i%4), i = 0..15.  The head reduce runs in VGPRs: each lane folds
-// its 16 heads (32 at 64 heads) into one partial with fma(w, max(acc, 0), p) in a fixed
-// order; the two half-waves are then added with v_permlane32_swap, which also packs two
+// 8*(i/4) + 4*(l/32) + (i%4), i = 0..15.  The head reduce runs in VGPRs in a fixed order
+// per lane; the two half-waves are then added with v_permlane32_swap, which also packs two
 // rows into one register (lanes 0-31 row A, lanes 32-63 row B).
 #pragma once
 #include "common.hpp"
@@ -99,97 +100,12 @@ struct KeyOperand {
   int sb[2];
 };
 
-// Load the operand of physical key `phys` from global memory.
-template <int FMT>
-__device__ __forceinline__ void load_key_global(KeyOperand& ko, const ScoreArgs& A, int64_t phys) {
-  constexpr int KB = Fmt<FMT>::kBytes;
-  const int half = lane_id() >> 5;
-  const uint8_t* kp = A.k + phys * KB;
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    if constexpr (FMT == FMT_E4M3) {
-      const v4i* src = reinterpret_cast<const v4i*>(kp + ks * 64 + half * 32);
-      const v4i x0 = src[0], x1 = src[1];
-      ko.b[ks] = v8i{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-      ko.sb[ks] = 127;
-    } else {
-      const v4i x = *reinterpret_cast<const v4i*>(kp + ks * 32 + half * 16);
-      ko.b[ks] = v8i{x.x, x.y, x.z, x.w, 0, 0, 0, 0};
-    }
-  }
-  if constexpr (FMT == FMT_MXFP4) {
-    const uint32_t sw = *reinterpret_cast<const uint32_t*>(A.k_sf + phys * 4);
-    ko.sb[0] = (sw >> (8 * half)) & 0xFF;
-    ko.sb[1] = (sw >> (8 * (2 + half))) & 0xFF;
-  }
-}
-
-// Load the operand from an LDS tile laid out as [key][stride bytes] (codes only) plus
-// the e8m0 scales of the key read from global memory.
-template <int FMT>
-__device__ __forceinline__ void load_key_lds(KeyOperand& ko, const uint8_t* row_lds, const ScoreArgs& A,
-                                             int64_t phys) {
-  const int half = lane_id() >> 5;
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    if constexpr (FMT == FMT_E4M3) {
-      const v4i* src = reinterpret_cast<const v4i*>(row_lds + ks * 64 + half * 32);
-      const v4i x0 = src[0], x1 = src[1];
-      ko.b[ks] = v8i{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-      ko.sb[ks] = 127;
-    } else {
-      const v4i x = *reinterpret_cast<const v4i*>(row_lds + ks * 32 + half * 16);
-      ko.b[ks] = v8i{x.x, x.y, x.z, x.w, 0, 0, 0, 0};
-    }
-  }
-  if constexpr (FMT == FMT_MXFP4) {
-    const uint32_t sw = *reinterpret_cast<const uint32_t*>(A.k_sf + phys * 4);
-    ko.sb[0] = (sw >> (8 * half)) & 0xFF;
-    ko.sb[1] = (sw >> (8 * (2 + half))) & 0xFF;
-  }
-}
-
-// max(x, 0) for finite x as one integer max on the bit pattern: non-negative floats have
-// non-negative int32 patterns in the same order, negative floats (and -0.0) negative ones,
-// so the result is x or +0.0.  Unlike fmaxf it needs no NaN-quieting canonicalisation.
-__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
-
-// Per-lane partial of sum_h w_h * max(dot_h, 0) over the heads this lane holds.
-template <int FMT, int H>
-__device__ __forceinline__ float row_partial(const RowOperand<FMT, H>& ro, const KeyOperand& ko) {
-  constexpr int C = Fmt<FMT>::kCode;
-  float p = 0.0f;
-#pragma unroll
-  for (int mt = 0; mt < RowOperand<FMT, H>::MT; ++mt) {
-    v16f acc = {};
-    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ro.a[mt][0], ko.b[0], acc, C, C, 0, ro.sa[mt][0], 0,
-                                                          ko.sb[0]);
-    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ro.a[mt][1], ko.b[1], acc, C, C, 0, ro.sa[mt][1], 0,
-                                                          ko.sb[1]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) p = __builtin_fmaf(ro.w[mt][i], relu(acc[i]), p);
-  }
-  return p;
-}
-
 // Add the two half-wave partials of row A (pa) and row B (pb): lanes 0-31 receive the
 // head sum of row A for key (l % 32), lanes 32-63 that of row B.  pa == pb gives the
 // single-row sum in every lane.
 __device__ __forceinline__ float combine_halves(float pa, float pb) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa), __float_as_uint(pb), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ float key_scale(const ScoreArgs& A, int64_t phys) {
-  return A.k_scale ? A.k_scale[phys] : 1.0f;
-}
-
-// Logical key s of row r -> physical key index (contiguous: s itself).
-__device__ __forceinline__ int64_t physical_key(const ScoreArgs& A, int r, int64_t s) {
-  if (!A.page_table) return s;
-  const int req = A.row_req[r];
-  const int32_t page = A.page_table[(int64_t)req * A.max_pages + (s >> 6)];
-  return (int64_t)page * kPage + (s & (kPage - 1));
 }
 
 }  // namespace idx

@@ -129,7 +129,7 @@ def test_score_workspace_and_check():
     assert lib.idx_score(ctypes.byref(p), out, 4096, ctypes.c_void_p(0x100080), need, None) == sai.IDX_EALIGN
     paged = _problem(rows=4, page_table=ctypes.c_void_p(0x30000), row_req=ctypes.c_void_p(0x30000), num_req=1,
                      max_pages=2, num_keys=128)
-    assert lib.idx_score_workspace(ctypes.byref(paged)) == 0
+    assert lib.idx_score_workspace(ctypes.byref(paged)) >= 4 * 660   # linear-tile pieces of every row
 
 
 def test_fused_workspace_grows_with_k_and_cap():

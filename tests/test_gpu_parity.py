@@ -161,6 +161,14 @@ def test_decode_family_reduced_paged():
     assert st["rows_store_all"] + st["rows_sampled"] == p.rows
 
 
+def test_paged_row_pairs_straddling_requests():
+    """Three rows per request: row pairs (0,1), (2,3), ... mix requests, so the paged kernel
+    scores such a pair one row at a time, each through its own request's pages."""
+    p = wl.decode(num_req=7, q_len=3, ctx_lo=2500, ctx_hi=30000, seed=17)
+    st = full_check(p, 1024, score_rows=range(p.rows))
+    assert st["rows_store_all"] + st["rows_sampled"] == p.rows
+
+
 # ----------------------------------------------------------------------------- edges
 
 def test_edge_lengths_e4m3():
