@@ -108,10 +108,17 @@ __device__ __forceinline__ void load_row_hist(SelSmem& sm, const uint32_t* gh) {
   __syncthreads();
 }
 
+// Elements above the boundary bin, and the bin's elements when they are kept for
+// refinement, are gathered in LDS first; one global atomic per workgroup and list then
+// reserves their places in the row's output and tie buffer.  At most m <= 2048 elements of
+// a row are above the bin (or in it, when it is selected whole) and at most kTieCap are in
+// it when ties are kept, so both lists fit.
+
 __global__ __launch_bounds__(kSelThreads) void mb_scatter_kernel(const float* x, int64_t ld,
                                                                  const int32_t* row_start, const int32_t* len,
                                                                  int32_t k, int32_t g, int32_t* out, SplitWs W) {
   __shared__ SelSmem sm;
+  __shared__ int32_t eidx[kMaxTopK];
   const int r = blockIdx.x / g, part = blockIdx.x % g;
   const int n = len[r];
   const int m = min(k, n);
@@ -122,10 +129,15 @@ __global__ __launch_bounds__(kSelThreads) void mb_scatter_kernel(const float* x,
   const uint32_t cnt = sm.bnd_count;
   const bool all_bin = cnt == (uint32_t)m - sm.bnd_above;
   const bool keep_ties = !all_bin && cnt <= (uint32_t)kTieCap;
+  if (threadIdx.x == 0) {
+    sm.nout = 0;
+    sm.ntie = 0;
+  }
+  __syncthreads();
   int lo, hi;
   segment(n, g, part, lo, hi);
   const int64_t off = (int64_t)r * ld + (row_start ? row_start[r] : 0);
-  int32_t* o = out + (int64_t)r * k;
+  const int l = lane_id();
   for (int base = lo; base < hi; base += kSelThreads) {
     const int j = base + (int)threadIdx.x;
     uint32_t key = 0, d = 0;
@@ -133,15 +145,35 @@ __global__ __launch_bounds__(kSelThreads) void mb_scatter_kernel(const float* x,
       key = order_key(x[off + j]);
       d = key >> (32 - kHistBits);
     }
-    const bool emit = j < hi && (d > b1 || (all_bin && d == b1));
-    const bool tie = j < hi && keep_ties && d == b1;
-    const int so = wave_append_slot(emit, &W.pos[r]);
-    if (emit) o[so] = j;
-    const int st = wave_append_slot(tie, &W.tcnt[r]);
-    if (tie) {
-      W.tkey[(int64_t)r * kTieCap + st] = key;
-      W.tidx[(int64_t)r * kTieCap + st] = j;
+    const uint64_t me = wave_ballot(j < hi && (d > b1 || (all_bin && d == b1)));
+    const uint64_t mt = wave_ballot(j < hi && keep_ties && d == b1);
+    int be = 0, bt = 0;
+    if (l == 0) {
+      if (me) be = atomicAdd(&sm.nout, __builtin_popcountll(me));
+      if (mt) bt = atomicAdd(&sm.ntie, __builtin_popcountll(mt));
     }
+    be = readlane(be, 0);
+    bt = readlane(bt, 0);
+    if ((me >> l) & 1) eidx[be + mask_prefix(me)] = j;
+    if ((mt >> l) & 1) {
+      const int t = bt + mask_prefix(mt);
+      sm.tkey[t] = key;
+      sm.tidx[t] = j;
+    }
+  }
+  __syncthreads();
+  const int ne = sm.nout, nt = sm.ntie;
+  if (threadIdx.x == 0) {
+    sm.bnd_bin = ne ? atomicAdd(&W.pos[r], ne) : 0;
+    sm.bnd_above = nt ? (uint32_t)atomicAdd(&W.tcnt[r], nt) : 0u;
+  }
+  __syncthreads();
+  const int ob = sm.bnd_bin, tb = (int)sm.bnd_above;
+  int32_t* o = out + (int64_t)r * k;
+  for (int t = threadIdx.x; t < ne; t += kSelThreads) o[ob + t] = eidx[t];
+  for (int t = threadIdx.x; t < nt; t += kSelThreads) {
+    W.tkey[(int64_t)r * kTieCap + tb + t] = sm.tkey[t];
+    W.tidx[(int64_t)r * kTieCap + tb + t] = sm.tidx[t];
   }
 }
 
