@@ -258,7 +258,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOADS[args.workload], "rows": p.rows, "key_scores": pairs, "k": k,
                    "heads": p.heads, "head_dim": 128, "format": p.fmt},
-        "roofline": {"bound": "mfma", "kernel": "score_kernel (fused score + filter)",
+        "roofline": {"bound": "mfma", "kernel": "score_tiles_kernel<MXFP4|e4m3, H, FILTER> (fused score + filter)",
                      "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "alg_flops_per_launch": alg_flops, "launch_ms": round(k2_ms, 4)},
