@@ -188,6 +188,23 @@ int idx_fused_topk(const idx_problem* p, int32_t k, int32_t* out_idx, void* ws, 
  * reads only the scalar fields of p).  Returns 0 for invalid arguments.            */
 size_t idx_fused_workspace(const idx_problem* p, int32_t k);
 
+/* ------------------------------------------------------------------ paged output
+ * idx_page_slots — selected logical positions to physical KV slots for a paged cache
+ * (LiteTopK page, section 3, topk_page_table_transform: a position pos >= 0 of request q
+ * becomes page_table[q][pos / 64] * 64 + pos % 64, and -1 passes through).
+ *   idx        int32 [rows][k]: indices relative to ks[r] (as idx_fused_topk and
+ *              idx_select return them), -1 for empty entries
+ *   ks         int32 [rows] first visible key of each row, or NULL for 0
+ *   page_table int32 [num_req][max_pages]; row_req int32 [rows] (as in idx_problem)
+ *   out        int32 [rows][k]; may equal idx (in place)
+ * For idx >= 0 the logical position is pos = ks[r] + idx; a pos whose page lies past
+ * max_pages yields -1 (no read outside the table).  Page entries the positions name must
+ * be valid.  One flat 1-D grid over rows * k; four entries per thread when k % 4 == 0
+ * and idx, out are 16-byte aligned.  Errors: IDX_EINVAL (null pointer with rows > 0,
+ * rows < 0, k < 1, max_pages < 1), IDX_EALIGN (idx or out not 4-byte aligned).       */
+int idx_page_slots(const int32_t* idx, int32_t rows, int32_t k, const int32_t* ks, const int32_t* page_table,
+                   const int32_t* row_req, int32_t max_pages, int32_t* out, void* stream);
+
 /* ------------------------------------------------------------------ measurement
  * Stage timing of idx_fused_topk for benchmarks.  While enabled, every idx_fused_topk
  * call (any thread) records six HIP events on its own stream at its stage boundaries,

@@ -79,6 +79,7 @@ def _lib():
             "idx_select_workspace": (sz, [i32, i64, i32]),
             "idx_fused_topk": (ctypes.c_int, [P, i32, _c_p, _c_p, sz, ctypes.POINTER(IdxStats), _c_p]),
             "idx_fused_workspace": (sz, [P, i32]),
+            "idx_page_slots": (ctypes.c_int, [_c_p, i32, i32, _c_p, _c_p, _c_p, i32, _c_p, _c_p]),
             "idx_strerror": (ctypes.c_char_p, [ctypes.c_int]),
             "idx_version": (i32, []),
             "idx_timing_enable": (ctypes.c_int, [i32]),
@@ -310,6 +311,19 @@ def idx_fused_topk(prob: DeviceProblem, k: int, stats: bool = False, stream=None
     """Exact top-k without materialising scores.  Returns out [rows, k] (and a stats dict)."""
     out, st = FusedRunner(prob, k)(stats=stats, stream=stream)
     return (out, st) if stats else out
+
+
+def idx_page_slots(idx: torch.Tensor, page_table: torch.Tensor, row_req: torch.Tensor,
+                   ks: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Physical KV slots of selected positions: out[r, j] = page_table[row_req[r], p // 64] * 64 + p % 64
+    with p = ks[r] + idx[r, j] (ks None: 0); -1 entries stay -1.  out may be idx (in place)."""
+    assert idx.dtype == torch.int32 and idx.dim() == 2 and idx.is_contiguous()
+    rows, k = idx.shape
+    if out is None:
+        out = torch.empty_like(idx)
+    _check(_lib().idx_page_slots(_ptr(idx), rows, k, _ptr(ks), _ptr(page_table), _ptr(row_req),
+                                 page_table.shape[1], _ptr(out), _stream(stream)), "idx_page_slots")
+    return out
 
 
 def version() -> int:

@@ -226,6 +226,20 @@ int idx_select(const float* scores, int64_t ld, const int32_t* row_start, const 
   return idx_select_split(scores, ld, row_start, len, rows, k, out_idx, ws, ws_bytes, g, stream);
 }
 
+int idx_page_slots(const int32_t* idx, int32_t rows, int32_t k, const int32_t* ks, const int32_t* page_table,
+                   const int32_t* row_req, int32_t max_pages, int32_t* out, void* stream) {
+  if (rows < 0 || k < 1 || max_pages < 1) return IDX_EINVAL;
+  if (rows == 0) return IDX_OK;
+  if (!idx || !page_table || !row_req || !out) return IDX_EINVAL;
+  if (!aligned(idx, 4) || !aligned(out, 4) || !aligned(page_table, 4) || !aligned(row_req, 4) ||
+      (ks && !aligned(ks, 4)))
+    return IDX_EALIGN;
+  int rc = current_device(nullptr);
+  if (rc) return rc;
+  return hip_err(launch_page_slots(idx, rows, k, ks, page_table, row_req, max_pages, out,
+                                   static_cast<hipStream_t>(stream)));
+}
+
 size_t idx_score_workspace(const idx_problem* p) {
   if (check_problem(p, nullptr) != IDX_OK) return 0;
   if (p->rows == 0) return 0;

@@ -54,6 +54,9 @@ void lin_carve(void* ws, int32_t rows, uint8_t** q8, uint8_t** sf);
 hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_idx, hipStream_t s,
                         hipEvent_t* ev = nullptr);
 
+hipError_t launch_page_slots(const int32_t* idx, int32_t rows, int32_t k, const int32_t* ks,
+                             const int32_t* page_table, const int32_t* row_req, int32_t max_pages, int32_t* out,
+                             hipStream_t s);
 hipError_t launch_select_single(const float* x, int64_t ld, const int32_t* row_start, const int32_t* len,
                                 int32_t rows, int32_t k, int32_t* out, hipStream_t s);
 hipError_t launch_select_split(const float* x, int64_t ld, const int32_t* row_start, const int32_t* len,

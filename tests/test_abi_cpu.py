@@ -24,7 +24,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("idx_score", "idx_score_workspace", "idx_select", "idx_fused_topk", "idx_select_workspace",
-              "idx_fused_workspace",
+              "idx_fused_workspace", "idx_page_slots",
               "idx_strerror", "idx_row_split", "idx_select_split", "idx_version"):
         assert n in names
 
@@ -166,3 +166,14 @@ def test_sample_stride_is_odd():
         p0 = _problem(rows=0)
         assert lib.idx_fused_topk(ctypes.byref(p0), k, None, None, 0, ctypes.byref(st), None) == 0
         assert st.sample_stride == s and st.sample_stride % 2 == 1
+
+
+def test_page_slots_argument_checks():
+    lib = sai.library()
+    a = ctypes.c_void_p(0x10000)
+    assert lib.idx_page_slots(a, -1, 4, None, a, a, 2, a, None) == sai.IDX_EINVAL
+    assert lib.idx_page_slots(a, 2, 0, None, a, a, 2, a, None) == sai.IDX_EINVAL
+    assert lib.idx_page_slots(a, 2, 4, None, a, a, 0, a, None) == sai.IDX_EINVAL
+    assert lib.idx_page_slots(None, 2, 4, None, a, a, 2, a, None) == sai.IDX_EINVAL
+    assert lib.idx_page_slots(ctypes.c_void_p(0x10002), 2, 4, None, a, a, 2, a, None) == sai.IDX_EALIGN
+    assert lib.idx_page_slots(None, 0, 4, None, None, None, 2, None, None) == 0    # nothing to do

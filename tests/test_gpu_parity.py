@@ -268,3 +268,36 @@ def test_fused_is_deterministic():
     a = np.sort(sai.idx_fused_topk(dp, 1024).cpu().numpy(), axis=1)
     b = np.sort(sai.idx_fused_topk(dp, 1024).cpu().numpy(), axis=1)
     assert np.array_equal(a, b)
+
+
+# ----------------------------------------------------------------------------- page slots
+
+def test_page_slots_golden_e6():
+    """Hand-worked page transform (LiteTopK page, section 3): page_row [7, 2]."""
+    g = golden("e6_page_transform.json")
+    pos = torch.tensor([g["pos"] + [0, 0, 0]], dtype=torch.int32).cuda()          # k = 8 (vector path)
+    pt = torch.tensor([g["page_row"]], dtype=torch.int32).cuda()
+    req = torch.zeros(1, dtype=torch.int32).cuda()
+    got = sai.idx_page_slots(pos, pt, req).cpu().numpy()[0]
+    assert got[:5].tolist() == g["slot"]
+    pos5 = torch.tensor([g["pos"]], dtype=torch.int32).cuda()                        # k = 5 (scalar path)
+    assert sai.idx_page_slots(pos5, pt, req).cpu().numpy()[0].tolist() == g["slot"]
+
+
+def test_page_slots_of_fused_decode_output():
+    """The fused top-k of a paged problem, mapped to physical slots, equals the oracle's
+    page transform of the oracle's selection on every row (ks offsets included)."""
+    p = wl.decode(num_req=5, ctx_lo=3000, ctx_hi=20000, seed=23)
+    p.ks = np.minimum(p.ks + 37, p.ke).astype(np.int32)                             # nonzero first keys
+    dp = dev(p)
+    sc, V = gpu_scores(dp, p)
+    ref_sel = oracle.select_rows(sc, V, 1024)
+    fused = sai.idx_fused_topk(dp, 1024)
+    got = sai.idx_page_slots(fused, dp.page_table, dp.row_req, ks=dp.ks).cpu().numpy()
+    for r in range(p.rows):
+        pos = np.where(ref_sel[r] >= 0, ref_sel[r] + p.ks[r], -1)
+        want = oracle.page_transform(pos, p.page_table[p.row_req[r]])
+        assert np.array_equal(np.sort(got[r]), np.sort(want)), r
+    inplace = fused.clone()
+    sai.idx_page_slots(inplace, dp.page_table, dp.row_req, ks=dp.ks, out=inplace)
+    assert np.array_equal(inplace.cpu().numpy(), got)
