@@ -30,9 +30,9 @@ constexpr int kThreads = 256;  // 4 waves per workgroup
 constexpr int kTile = 32;      // keys per MFMA block
 
 // Rows per workgroup: 4 waves x RowsPerWave (contiguous kernel: 4 rows per wave for MXFP4
-// at 32 heads, else 2); the paged kernel holds one row pair in all four waves.
+// at 32 heads, else 2); the paged kernel takes a row quad (see score_pages_kernel).
 int rows_per_block(int heads, int fmt) { return 4 * (heads == 32 && fmt == FMT_MXFP4 ? 4 : 2); }
-static int rows_per_block_paged(int) { return 2; }  // score_pages_kernel: one row pair
+static int rows_per_block_paged(int) { return 4; }  // score_pages_kernel: one row quad
 static int rows_per_block_for(const DevProblem& P) {
   return P.page_table ? rows_per_block_paged(P.heads) : rows_per_block(P.heads, P.fmt);
 }
@@ -342,7 +342,13 @@ struct StageLds {
   float* ks;       // [2][kKeys] half the per-key scale (0.5 when absent)
   float* cand_s;   // FILTER: [waves][RW][kCandBuf] candidate scores of this workgroup's rows
   int32_t* cand_i; //         and their key indices relative to ks
+  int32_t* pages;  // paged: kPageCache page ids of the call's key range (nullptr: read the table)
 };
+
+// Paged keys: page ids a score call touches are read from the page table once, into LDS,
+// instead of before every stage's key loads.  2560 ids cover a 16384-key chunk, or 2048
+// sample slots at the largest sample stride (71 keys apart).
+constexpr int kPageCache = 2560;
 
 // FILTER mode: each wave collects its candidates in an LDS buffer of its own (no LDS
 // atomics) and moves them to the global slab in batches, with one global atomic per row
@@ -353,13 +359,16 @@ constexpr int kCandBuf = 256;
 // (positions: keys, or sample slots with key = phase + pos * S), with the epilogue of MODE.
 // Every wave of the workgroup must call it with the same tA, tB.  Default: every wave has
 // rows of its own and scores every tile that meets them.  SHARED: all waves hold the same
-// rows and wave w scores tiles w and w + 4 of each stage (paged keys, the fallback).
-// rmask selects the rows that count (the others see no keys); req >= 0 reads keys through
-// request req's page table.  MODE_ROWSTORE writes only row E.only_row, to E.out[key - ks].
+// rows and wave w scores tiles w and w + 4 of each stage (paged keys, the fallback); with
+// split = 2 two waves share rows and take alternate tiles (slot = which of them).  rmask
+// selects the rows that count (the others see no keys); req >= 0 reads keys through
+// request req's page table, clamped to klim when given (else to this wave's rows' last
+// visible key).  MODE_ROWSTORE writes only row E.only_row, to E.out[key - ks].
 template <int FMT, int H, int MODE, int RW, bool SHARED>
 __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, const EpiArgs& E, int row0,
                                          int phase, int S, int c0, int c1, int tA, int tB,
-                                         const StageLds<FMT>& sl, int req = -1, uint32_t rmask = ~0u) {
+                                         const StageLds<FMT>& sl, int req = -1, uint32_t rmask = ~0u,
+                                         int split = 4, int slot = -1, int64_t klim = -1) {
   static_assert(RW % 2 == 0, "rows are processed in pairs");
   using G = StageGeom<FMT>;
   constexpr int KB = G::kKB;
@@ -419,11 +428,33 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
   // Physical key of stage position pos: contiguous keys are clamped to the key array;
   // paged keys (all rows of request `req`) are clamped to the rows' visible range, then
   // mapped through the request's page table (64 keys per page).
+  // Paged: cache the page ids of every logical key the stage loads can reach (positions
+  // [tA * kTile, tA * kTile + nst * kKeys), clamped to lmax like key_of) when they fit.
+  int64_t pg_lo = 0;
+  bool pg_cached = false;
+  if (klim >= 0) lmax = (int)klim;  // the workgroup's key limit (waves with different rows)
+  if (req >= 0 && sl.pages) {
+    const int64_t nst_keys = (int64_t)((tB - tA + G::kTiles - 1) / G::kTiles) * G::kKeys;
+    int64_t k_first = (int64_t)phase + (int64_t)tA * kTile * S;
+    int64_t k_last = (int64_t)phase + ((int64_t)tA * kTile + nst_keys - 1) * S;
+    k_first = k_first < lmax ? k_first : lmax;
+    k_last = k_last < lmax ? k_last : lmax;
+    pg_lo = k_first >> 6;
+    const int64_t npg = (k_last >> 6) - pg_lo + 1;
+    pg_cached = npg <= kPageCache;  // workgroup-uniform
+    if (pg_cached) {
+      for (int64_t j = threadIdx.x; j < npg; j += kThreads)
+        sl.pages[j] = A.page_table[(int64_t)req * A.max_pages + pg_lo + j];
+      __syncthreads();
+    }
+  }
   auto key_of = [&](int64_t pos) -> int64_t {
     const int64_t key = (int64_t)phase + pos * S;
     if (req < 0) return key < last_key ? key : last_key;
     const int64_t lk = key < lmax ? key : lmax;
-    return (int64_t)A.page_table[(int64_t)req * A.max_pages + (lk >> 6)] * kPage + (lk & (kPage - 1));
+    const int64_t page = lk >> 6;
+    const int32_t id = pg_cached ? sl.pages[page - pg_lo] : A.page_table[(int64_t)req * A.max_pages + page];
+    return (int64_t)id * kPage + (lk & (kPage - 1));
   };
 
   // FILTER: this wave's LDS candidate buffers and their (wave-uniform) fill counts.
@@ -627,7 +658,7 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
     for (int i = 0; i < G::kTiles; ++i) {
       const int t = tbase + i;
       if (t >= tB) break;  // workgroup-uniform
-      const bool mine = SHARED ? ((i & 3) == wave) : (t >= wt0 && t < wt1);
+      const bool mine = SHARED ? ((i % split) == (slot < 0 ? wave : slot)) : (t >= wt0 && t < wt1);
       if (mine) compute(buf, i, t);
     }
     if (more) lwrite(buf ^ 1);
@@ -692,32 +723,35 @@ __global__ __launch_bounds__(kThreads, 2) void score_tiles_kernel(ScoreArgs A, L
   wg_tiles<FMT, H, MODE, RW, false>(A, L, E, rb * 4 * RW + wave * RW, phase, S, c0, c1, tA, tB, sl);
 }
 
-// Paged keys: one workgroup per (row pair, key chunk).  The pair's rows must read the same
-// request's pages to share the LDS stage, so a pair that straddles two requests is scored
-// in two passes, one row each.  All four waves hold the pair and split each stage's tiles.
+// Paged keys: one workgroup per (row quad, key chunk).  Rows must read one request's pages
+// to share the LDS stage.  When all four rows belong to one request (MTP decode rows), the
+// two row pairs share each stage: waves 0/1 hold the pairs and take even tiles, waves 2/3
+// the odd ones.  Otherwise each pair is scored on its own with all four waves holding it,
+// and a pair that straddles two requests in two one-row passes.
 template <int FMT, int H, int MODE>
 __global__ __launch_bounds__(kThreads, 2) void score_pages_kernel(ScoreArgs A, LinArgs L, EpiArgs E, TileWork W) {
   __shared__ StageShared<FMT> sh;
   __shared__ CandShared<2, MODE == MODE_FILTER> cand;
+  __shared__ int32_t pages[kPageCache];
   const int64_t item = map_item(W);
   if (item >= W.total) return;
-  const int pr = (int)(item % W.nrb);
+  const int rb = (int)(item % W.nrb);
   const int chunk = (int)(item / W.nrb);
-  const int row0 = 2 * pr;
+  const int base = 4 * rb;
   const int S = (MODE == MODE_SAMPLE) ? E.stride : 1;
-  const int phase = (MODE == MODE_SAMPLE) ? sample_phase(pr, S) : 0;
+  const int phase = (MODE == MODE_SAMPLE) ? sample_phase(rb, S) : 0;
   const int c0 = chunk * W.chunk, c1 = c0 + W.chunk;
-  const bool two = row0 + 1 < A.rows;
-  const int q0 = A.row_req[row0], q1 = two ? A.row_req[row0 + 1] : q0;
-  const StageLds<FMT> sl{sh.codes, sh.sf, sh.ks, cand.s, cand.i};
-  for (int pass = 0; pass < (q0 == q1 ? 1 : 2); ++pass) {  // workgroup-uniform
-    const uint32_t rmask = q0 == q1 ? 3u : (1u << pass);
-    const int req = pass == 0 ? q0 : q1;
+  const int wave = uniform(threadIdx.x / kWave);
+  const StageLds<FMT> sl{sh.codes, sh.sf, sh.ks, cand.s, cand.i, pages};
+  // Tile range of the given rows within the chunk (positions: keys or sample slots).
+  auto span = [&](int r0, int n, uint32_t rmask, int& tA, int& tB, int& kmax) {
     int lo = 0x7FFFFFFF, hi = 0;
-    for (int i = 0; i < 2; ++i) {
-      const int r = row0 + i;
+    kmax = 0;
+    for (int i = 0; i < n; ++i) {
+      const int r = r0 + i;
       if (r >= A.rows || !((rmask >> i) & 1)) continue;
       const int ks = A.ks[r], ke = A.ke[r];
+      kmax = max(kmax, ke - 1);
       int plo = ks, phi = ke;
       if (MODE == MODE_SAMPLE) {
         plo = phi = 0;
@@ -728,9 +762,33 @@ __global__ __launch_bounds__(kThreads, 2) void score_pages_kernel(ScoreArgs A, L
         hi = max(hi, phi);
       }
     }
-    const int tA = max(c0, lo) / kTile, tB = (min(c1, hi) + kTile - 1) / kTile;
-    if (tA < tB) wg_tiles<FMT, H, MODE, 2, true>(A, L, E, row0, phase, S, c0, c1, tA, tB, sl, req, rmask);
-    __syncthreads();
+    tA = max(c0, lo) / kTile;
+    tB = (min(c1, hi) + kTile - 1) / kTile;
+  };
+  const int nr = min(4, A.rows - base);
+  bool one_req = nr == 4;
+  for (int i = 1; i < nr && one_req; ++i) one_req = A.row_req[base + i] == A.row_req[base];
+  if (one_req) {
+    int tA, tB, kmax;
+    span(base, 4, 0xFu, tA, tB, kmax);
+    if (tA < tB)
+      wg_tiles<FMT, H, MODE, 2, true>(A, L, E, base + 2 * (wave & 1), phase, S, c0, c1, tA, tB, sl,
+                                      A.row_req[base], ~0u, 2, wave >> 1, kmax);
+    return;
+  }
+  for (int pr = 0; pr < 2; ++pr) {  // workgroup-uniform
+    const int row0 = base + 2 * pr;
+    if (row0 >= A.rows) break;
+    const bool two = row0 + 1 < A.rows;
+    const int q0 = A.row_req[row0], q1 = two ? A.row_req[row0 + 1] : q0;
+    for (int pass = 0; pass < (q0 == q1 ? 1 : 2); ++pass) {
+      const uint32_t rmask = q0 == q1 ? 3u : (1u << pass);
+      int tA, tB, kmax;
+      span(row0, 2, rmask, tA, tB, kmax);
+      if (tA < tB)
+        wg_tiles<FMT, H, MODE, 2, true>(A, L, E, row0, phase, S, c0, c1, tA, tB, sl, pass == 0 ? q0 : q1, rmask);
+      __syncthreads();
+    }
   }
 }
 
