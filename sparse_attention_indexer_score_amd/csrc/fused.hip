@@ -91,12 +91,18 @@ struct TileWork {
   int64_t total;   // nrb * nchunk
 };
 
-// Workgroup -> (row block, chunk).  Workgroups are dealt to the 8 XCDs round-robin, so
-// workgroup b runs on XCD b % 8; all row blocks of one chunk go to the same XCD, back to
-// back, and the chunk's keys are fetched into that XCD's L2 once.
+// Workgroup -> work item (item = chunk * nrb + row block).  Workgroups are dealt to the 8
+// XCDs round-robin, so workgroup b runs on XCD b % 8.
+//  - At least 8 chunks: chunk c runs on XCD c % 8, its row blocks back to back, so its keys
+//    are fetched into that XCD's L2 once and the chunks near the start of the key range,
+//    which short rows still reach, are spread over all XCDs.  Grid: ceil(nchunk / 8) * 8
+//    * nrb workgroups.
+//  - Fewer chunks: XCD x takes the x-th eighth of the items, so every XCD has work.  Grid:
+//    8 * ceil(total / 8) workgroups.
 __device__ __forceinline__ int64_t map_item(const TileWork& W) {
   const int64_t b = blockIdx.x;
   const int64_t x = b & 7, local = b >> 3;
+  if (W.nchunk < 8) return x * ((W.total + 7) / 8) + local;
   const int64_t g = local / W.nrb, j = local % W.nrb;
   return (g * 8 + x) * W.nrb + j;
 }
@@ -1042,8 +1048,8 @@ static TileWork tile_work(const DevProblem& P, int64_t positions, int chunk) {
 }
 
 static dim3 tile_grid(const TileWork& W) {
-  const int64_t groups = (W.nchunk + 7) / 8;
-  return dim3((unsigned)(groups * 8 * W.nrb));
+  if (W.nchunk < 8) return dim3((unsigned)(8 * ((W.total + 7) / 8)));
+  return dim3((unsigned)((W.nchunk + 7) / 8 * 8 * W.nrb));
 }
 
 static LinArgs lin_args(const FusedPlan& F) { return LinArgs{F.lin_q8, F.lin_sf}; }
