@@ -85,8 +85,10 @@ typedef struct idx_debug {
  *            (LiteTopK page, section 3).  Entries past a request's last visible page are
  *            never read.
  *   row_req  paged only: int32 [rows], request of each row, in [0, num_req).
+ *   num_keys must be > 0 when rows > 0 (IDX_EINVAL otherwise).
  *   Values the library cannot check on the host (ranges inside device arrays, NaN
- *   codes, page ids) must be valid; invalid ones give undefined results.
+ *   codes, page ids) must be valid; invalid ones give undefined results, but key reads
+ *   stay inside k and the page table (out-of-range keys and slots are clamped).
  */
 typedef struct idx_problem {
   int32_t rows;

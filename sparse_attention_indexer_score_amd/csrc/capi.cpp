@@ -59,9 +59,7 @@ int check_problem(const idx_problem* p, DevProblem* out) {
   }
   if (p->rows > 0) {
     if (!p->q || !p->k || !p->w || !p->ks || !p->ke) return IDX_EINVAL;
-    if (p->num_keys == 0 && !paged) {
-      // rows may still be empty (ks == ke); the kernels never read k then
-    }
+    if (p->num_keys == 0) return IDX_EINVAL;  // the kernels clamp key reads into [0, num_keys)
   }
   if (paged) {
     if (!p->row_req || p->num_req <= 0 || p->max_pages <= 0 || (p->num_keys % IDX_PAGE) != 0) return IDX_EINVAL;

@@ -434,11 +434,18 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
   // Physical key of stage position pos: contiguous keys are clamped to the key array;
   // paged keys (all rows of request `req`) are clamped to the rows' visible range, then
   // mapped through the request's page table (64 keys per page).
+  // Page ids outside the key array (invalid input) are clamped so reads stay inside K.
+  const int32_t last_page = (int32_t)(A.num_keys / kPage) - 1;
+  auto valid_page = [&](int32_t id) -> int32_t { return id < 0 ? 0 : (id > last_page ? last_page : id); };
   // Paged: cache the page ids of every logical key the stage loads can reach (positions
   // [tA * kTile, tA * kTile + nst * kKeys), clamped to lmax like key_of) when they fit.
   int64_t pg_lo = 0;
   bool pg_cached = false;
   if (klim >= 0) lmax = (int)klim;  // the workgroup's key limit (waves with different rows)
+  if (req >= 0) {  // logical keys past the page table (ke beyond max_pages pages) stay inside it
+    const int64_t table_keys = (int64_t)A.max_pages * kPage - 1;
+    lmax = lmax < table_keys ? lmax : (int)table_keys;
+  }
   if (req >= 0 && sl.pages) {
     const int64_t nst_keys = (int64_t)((tB - tA + G::kTiles - 1) / G::kTiles) * G::kKeys;
     int64_t k_first = (int64_t)phase + (int64_t)tA * kTile * S;
@@ -450,7 +457,7 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
     pg_cached = npg <= kPageCache;  // workgroup-uniform
     if (pg_cached) {
       for (int64_t j = threadIdx.x; j < npg; j += kThreads)
-        sl.pages[j] = A.page_table[(int64_t)req * A.max_pages + pg_lo + j];
+        sl.pages[j] = valid_page(A.page_table[(int64_t)req * A.max_pages + pg_lo + j]);
       __syncthreads();
     }
   }
@@ -459,7 +466,7 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
     if (req < 0) return key < last_key ? key : last_key;
     const int64_t lk = key < lmax ? key : lmax;
     const int64_t page = lk >> 6;
-    const int32_t id = pg_cached ? sl.pages[page - pg_lo] : A.page_table[(int64_t)req * A.max_pages + page];
+    const int32_t id = pg_cached ? sl.pages[page - pg_lo] : valid_page(A.page_table[(int64_t)req * A.max_pages + page]);
     return (int64_t)id * kPage + (lk & (kPage - 1));
   };
 

@@ -86,6 +86,7 @@ def _problem(**kw):
     (dict(q=ctypes.c_void_p(0x10008)), sai.IDX_EALIGN),            # q must be 16-byte aligned
     (dict(ks=ctypes.c_void_p(0x10002)), sai.IDX_EALIGN),
     (dict(page_table=ctypes.c_void_p(0x30000)), sai.IDX_EINVAL),   # paged without row_req
+    (dict(num_keys=0), sai.IDX_EINVAL),                              # rows but no keys to read
 ])
 def test_problem_validation_on_host(mut, code):
     lib = sai.library()
