@@ -736,6 +736,13 @@ __global__ __launch_bounds__(kThreads, 2) void score_tiles_kernel(ScoreArgs A, L
   wg_tiles<FMT, H, MODE, RW, false>(A, L, E, rb * 4 * RW + wave * RW, phase, S, c0, c1, tA, tB, sl);
 }
 
+// Request of a paged row, clamped to [0, num_req) so an invalid id cannot read outside
+// the page table.
+__device__ __forceinline__ int request_of(const ScoreArgs& A, int r) {
+  const int q = A.row_req[r];
+  return q < 0 ? 0 : (q >= A.num_req ? A.num_req - 1 : q);
+}
+
 // Paged keys: one workgroup per (row quad, key chunk).  Rows must read one request's pages
 // to share the LDS stage.  When all four rows belong to one request (MTP decode rows), the
 // two row pairs share each stage: waves 0/1 hold the pairs and take even tiles, waves 2/3
@@ -780,20 +787,20 @@ __global__ __launch_bounds__(kThreads, 2) void score_pages_kernel(ScoreArgs A, L
   };
   const int nr = min(4, A.rows - base);
   bool one_req = nr == 4;
-  for (int i = 1; i < nr && one_req; ++i) one_req = A.row_req[base + i] == A.row_req[base];
+  for (int i = 1; i < nr && one_req; ++i) one_req = request_of(A, base + i) == request_of(A, base);
   if (one_req) {
     int tA, tB, kmax;
     span(base, 4, 0xFu, tA, tB, kmax);
     if (tA < tB)
       wg_tiles<FMT, H, MODE, 2, true>(A, L, E, base + 2 * (wave & 1), phase, S, c0, c1, tA, tB, sl,
-                                      A.row_req[base], ~0u, 2, wave >> 1, kmax);
+                                      request_of(A, base), ~0u, 2, wave >> 1, kmax);
     return;
   }
   for (int pr = 0; pr < 2; ++pr) {  // workgroup-uniform
     const int row0 = base + 2 * pr;
     if (row0 >= A.rows) break;
     const bool two = row0 + 1 < A.rows;
-    const int q0 = A.row_req[row0], q1 = two ? A.row_req[row0 + 1] : q0;
+    const int q0 = request_of(A, row0), q1 = two ? request_of(A, row0 + 1) : q0;
     for (int pass = 0; pass < (q0 == q1 ? 1 : 2); ++pass) {
       const uint32_t rmask = q0 == q1 ? 3u : (1u << pass);
       int tA, tB, kmax;
@@ -1009,7 +1016,7 @@ __global__ __launch_bounds__(kThreads) void fallback_tiles_kernel(ScoreArgs A, L
       EpiArgs E = {};
       E.out = mine;
       E.only_row = r;
-      const int req = A.page_table ? A.row_req[r] : -1;
+      const int req = A.page_table ? request_of(A, r) : -1;
       wg_tiles<FMT, H, MODE_ROWSTORE, RW, true>(A, L, E, (r / RW) * RW, 0, 1, ks, ke, ks / kTile,
                                                 (ke + kTile - 1) / kTile, sl, req, 1u << (r % RW));
     }
@@ -1037,6 +1044,7 @@ static ScoreArgs score_args(const DevProblem& P) {
   A.page_table = P.page_table;
   A.row_req = P.row_req;
   A.max_pages = P.max_pages;
+  A.num_req = P.num_req;
   A.rows = P.rows;
   A.num_keys = P.num_keys;
   return A;

@@ -48,6 +48,7 @@ struct ScoreArgs {
   const int32_t* page_table;
   const int32_t* row_req;
   int32_t max_pages;
+  int32_t num_req;
   int32_t rows;
   int64_t num_keys;  // physical keys (contiguous) or slots (paged)
 };

@@ -161,6 +161,20 @@ def test_decode_family_reduced_paged():
     assert st["rows_store_all"] + st["rows_sampled"] == p.rows
 
 
+def test_mxfp4_64_heads():
+    """MXFP4 keys with 64 heads (two rows per wave, two head tiles per row)."""
+    p = wl.long_context(rows=40, num_keys=20000, heads=64, band_keys=3000, seed=31)
+    st = full_check(p, 1024, score_rows=range(0, 40, 6))
+    assert st["rows_sampled"] + st["rows_store_all"] == p.rows
+
+
+def test_paged_32_heads():
+    """Paged e4m3 keys with 32 heads."""
+    p = wl.decode(num_req=5, ctx_lo=3000, ctx_hi=25000, heads=32, seed=37)
+    st = full_check(p, 2048, score_rows=range(0, p.rows, 3))
+    assert st["rows_sampled"] + st["rows_store_all"] == p.rows
+
+
 def test_paged_row_pairs_straddling_requests():
     """Three rows per request: row pairs (0,1), (2,3), ... mix requests, so the paged kernel
     scores such a pair one row at a time, each through its own request's pages."""
