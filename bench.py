@@ -156,6 +156,34 @@ def secondary_legs(dev, iters=20):
     return res
 
 
+def routing_table(dev, rows=2048, contexts=(4096, 8192, 16384, 32768, 65536, 131072), k=2048, iters=10):
+    """Dense path (idx_score writes every score, idx_select reads them back) against the fused
+    path on the prefill family (e4m3, 64 heads, causal) at a fixed batch and growing context,
+    to locate the crossover.  Returns one record per context length."""
+    import torch
+    import sparse_attention_indexer_score_amd as sai
+    from sparse_attention_indexer_score_amd import workloads as wl
+    out = []
+    for n in contexts:
+        p = wl.prefill(rows=rows, num_keys=n, topk=k, seed=3)
+        dp = sai.DeviceProblem.from_host(p, dev)
+        fused = sai.FusedRunner(dp, k)
+        sr = sai.ScoreRunner(dp, ld=int((p.ke - p.ks).max()))
+        sel = sai.SelectRunner(sr.out, (dp.ke - dp.ks).to(torch.int32), k)
+        dense = lambda: (sr(), sel())
+        fused(); dense()
+        torch.cuda.synchronize()
+        f_ms, _ = timed_ms(fused, iters)
+        d_ms, _ = timed_ms(dense, iters)
+        rec = {"keys": n, "rows": rows, "pairs": int(p.pairs), "fused_ms": round(f_ms, 4), "dense_ms": round(d_ms, 4),
+               "fused_over_dense_speedup": round(d_ms / f_ms, 3)}
+        log(f"[routing] {rec}")
+        out.append(rec)
+        del fused, sr, sel, dp
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,6 +191,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-rows", type=int, default=16, help="rows in the oracle's timed sample (0: skip)")
+    ap.add_argument("--routing", action="store_true",
+                    help="only measure dense (idx_score + idx_select) against fused top-k over context lengths")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the selection and materialised-score measurements")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -170,13 +200,22 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (rows shard with no "
-              "communication; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: there is no multi-GPU path (rows would shard across GPUs "
+              "with no communication). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
     import sparse_attention_indexer_score_amd as sai
     from sparse_attention_indexer_score_amd import workloads as wl
+
+    if args.routing:
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        table = routing_table(dev)
+        print(json.dumps({"metric": "fused vs dense indexer top-k ms by context length (prefill family, 2048 rows, "
+                                    "e4m3, 64 heads, k=2048), 1 GPU", "n_gpus": 1, "data": "synthetic",
+                          "higher_is_better": False, "table": table}), flush=True)
+        return
 
     log(f"[bench] generating workload '{args.workload}'")
     t = time.perf_counter()

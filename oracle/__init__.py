@@ -27,7 +27,7 @@ What it computes, and where that is defined
 * Paged K (LiteTopK page, section 3, topk_page_table_transform): logical position s of
   a request lives in physical slot page_table[req][s // 64] * 64 + s % 64.
 
-Readings where the pages are silent (each is also listed in the design notes):
+Readings where the pages are silent:
 * e4m3 is OCP E4M3FN (bias 7, no infinities, 0x7F/0xFF NaN); MXFP4 is OCP e2m1 with
   one e8m0 scale per 32 consecutive head_dim elements, element 2i in the low nibble.
 * A per-key fp32 scale multiplies the decoded key vector (equivalently the score,
