@@ -501,10 +501,10 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
   };
 
   // Epilogue of one tile for every row pair, given the pairs' packed scores.
-  auto epilogue = [&](int t, const float* score_of) {
+  auto epilogue = [&](int t, const float* score_of, bool known_full) {
     const int pos = t * kTile + col;
     const int64_t key = (int64_t)phase + (int64_t)pos * S;
-    const bool full = t * kTile >= full_lo && (t + 1) * kTile <= full_hi;  // wave-uniform
+    const bool full = known_full || (t * kTile >= full_lo && (t + 1) * kTile <= full_hi);  // wave-uniform
     if constexpr (MODE == MODE_FILTER) {
       // One compare and ballot per row pair; the append path runs only for the (rare)
       // tiles that hold a candidate.
@@ -615,7 +615,7 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
       sc[p] = finish_score2(combine_halves(part[2 * p], part[2 * p + 1]), lin_of_pair(a.lin, p), half_kscale);
   };
   // One tile: key operand from LDS, MFMAs for all RW rows and the linear tile, reduce, epilogue.
-  auto compute = [&](int buf, int i, int t) {
+  auto compute = [&](int buf, int i, int t, bool known_full) {
     KeyOperand ko;
     float ksc;
     read_b(buf, i, ko, ksc);
@@ -623,7 +623,7 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
     issue(a, ko);
     float sc[NP];
     reduce(a, ksc, sc);
-    epilogue(t, sc);
+    epilogue(t, sc, known_full);
   };
 
   // Stage loads: thread c of the workgroup fetches 16-byte pieces c, c + 256, ... of the
@@ -667,12 +667,23 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
     const bool more = st + 1 < nst;
     if (more) gload(st + 1);
     const int tbase = tA + st * G::kTiles;
+    bool whole = false;  // wave-uniform: every tile of the stage is this wave's and inside all its rows
+    if constexpr (!SHARED && RW >= 4)  // (a second copy of the tile loop; 2-row kernels lack the registers)
+      whole = tbase >= wt0 && tbase + G::kTiles <= min(wt1, tB) && tbase * kTile >= full_lo &&
+              (tbase + G::kTiles) * kTile <= full_hi;
+    if (whole) {
+      if constexpr (!SHARED && RW >= 4) {
 #pragma unroll
-    for (int i = 0; i < G::kTiles; ++i) {
-      const int t = tbase + i;
-      if (t >= tB) break;  // workgroup-uniform
-      const bool mine = SHARED ? ((i % split) == (slot < 0 ? wave : slot)) : (t >= wt0 && t < wt1);
-      if (mine) compute(buf, i, t);
+        for (int i = 0; i < G::kTiles; ++i) compute(buf, i, tbase + i, true);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < G::kTiles; ++i) {
+        const int t = tbase + i;
+        if (t >= tB) break;  // workgroup-uniform
+        const bool mine = SHARED ? ((i % split) == (slot < 0 ? wave : slot)) : (t >= wt0 && t < wt1);
+        if (mine) compute(buf, i, t, false);
+      }
     }
     if (more) lwrite(buf ^ 1);
     __syncthreads();

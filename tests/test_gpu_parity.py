@@ -1,6 +1,6 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
 
-Bars (the tolerance is the one the target statement fixes for fp32 scores):
+Bars:
 * integer-valued e4m3 inputs: scores bit-exact, index sets bit-exact;
 * real-valued inputs: |gpu - oracle| <= 1e-4 + 1e-5 * |oracle| per score; selection over
   the GPU's own scores bit-exact (oracle select == idx_select == idx_fused_topk), which
