@@ -324,9 +324,9 @@ __device__ __forceinline__ float finish_score2(float abs_sum, float lin, float h
 }
 
 // Key tiles are staged through LDS: all four waves of a workgroup use the same keys, so a
-// stage of 32-key tiles is fetched once per workgroup with coalesced 16-byte loads (issued
-// one stage ahead, double-buffered, one barrier per stage) and each wave reads its MFMA key
-// operands from LDS.  Rows are padded to KB + 16 bytes so that the 8 lanes of a 16-byte LDS
+// stage of 32-key tiles is fetched once per workgroup with 16-byte loads straight into LDS
+// (issued one stage ahead, double-buffered, one barrier per stage) and each wave reads its
+// MFMA key operands from LDS.  Rows are padded to KB + 16 bytes so that the 8 lanes of a 16-byte LDS
 // read phase hit distinct banks.  A stage is 8 tiles of 80-byte fp4 rows or 4 tiles of
 // 144-byte e4m3 rows, which keeps two workgroups per CU within LDS.
 template <int FMT>
@@ -336,9 +336,6 @@ struct StageGeom {
   static constexpr int kStride = kKB + 16;
   static constexpr int kKeys = kTiles * kTile;             // keys per stage
   static constexpr int kBytes = kKeys * kStride;           // codes of one stage
-  static constexpr int kChunks = kKeys * kKB / 16;          // 16-byte loads per stage
-  static constexpr int kPerThread = kChunks / kThreads;     // fp4: 4, fp8: 4
-  static_assert(kChunks % kThreads == 0, "stage must split evenly");
 };
 
 template <int FMT>
@@ -576,7 +573,7 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
       ko.sb[0] = (sw >> (8 * half)) & 0xFF;
       ko.sb[1] = (sw >> (8 * (2 + half))) & 0xFF;
     }
-    half_kscale = sl.ks[buf * G::kKeys + kidx];
+    half_kscale = A.k_scale ? 0.5f * sl.ks[buf * G::kKeys + kidx] : 0.5f;
   };
   struct Acc {
     v16f row[RW][H / 32];
@@ -626,46 +623,51 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
     epilogue(t, sc, known_full);
   };
 
-  // Stage loads: thread c of the workgroup fetches 16-byte pieces c, c + 256, ... of the
-  // stage's key codes, and the block-scale word and key scale of key c (c < 128).
-  v4i regs[G::kPerThread];
-  uint32_t sfw = 0;
-  float ksv = 1.0f;
-  auto gload = [&](int stage) {
+  // Stage loads straight into LDS (global_load_lds_dwordx4): lane l of wave w writes the 16
+  // bytes it fetches to the wave's LDS base + 16 l, so each lane is given the global piece
+  // that belongs in its 16-byte slot of the padded [key][kStride] layout (a pad slot fetches
+  // part 0 of its key again).  Block scales and key scales come by 4-byte loads.
+  constexpr int kSlotsPerKey = G::kStride / 16;
+  constexpr int kSlots = G::kKeys * kSlotsPerKey;
+  constexpr int kSlotIters = (kSlots + kThreads - 1) / kThreads;
+  const bool has_ks = A.k_scale != nullptr;
+  auto dma = [&](int stage, int buf) {
     const int64_t pos0 = (int64_t)(tA + stage * G::kTiles) * kTile;
+    uint8_t* lbase = sl.codes + buf * G::kBytes;
 #pragma unroll
-    for (int u = 0; u < G::kPerThread; ++u) {
-      const int c = threadIdx.x + u * kThreads;
-      const int key = c / (KB / 16), part = c % (KB / 16);
-      regs[u] = *reinterpret_cast<const v4i*>(A.k + key_of(pos0 + key) * KB + part * 16);
+    for (int u = 0; u < kSlotIters; ++u) {
+      const int s0 = u * kThreads + wave * kWave;
+      if (s0 < kSlots) {  // wave-uniform
+        const int sidx = s0 + l;
+        const int key = sidx / kSlotsPerKey, part = sidx % kSlotsPerKey;
+        const int pp = part < KB / 16 ? part : 0;
+        const uint8_t* src = A.k + key_of(pos0 + key) * KB + pp * 16;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                         (__attribute__((address_space(3))) void*)(lbase + s0 * 16), 16, 0, 0);
+      }
     }
-    if (threadIdx.x < G::kKeys) {
-      const int64_t g = key_of(pos0 + threadIdx.x);
-      if constexpr (FMT == FMT_MXFP4) sfw = *reinterpret_cast<const uint32_t*>(A.k_sf + g * 4);
-      ksv = A.k_scale ? A.k_scale[g] : 1.0f;
-    }
-  };
-  auto lwrite = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < G::kPerThread; ++u) {
-      const int c = threadIdx.x + u * kThreads;
-      const int key = c / (KB / 16), part = c % (KB / 16);
-      *reinterpret_cast<v4i*>(sl.codes + buf * G::kBytes + key * G::kStride + part * 16) = regs[u];
-    }
-    if (threadIdx.x < G::kKeys) {
-      sl.sf[buf * G::kKeys + threadIdx.x] = sfw;
-      sl.ks[buf * G::kKeys + threadIdx.x] = 0.5f * ksv;
+    if (wave * kWave < G::kKeys) {  // wave-uniform
+      const int key = wave * kWave + l;
+      const int64_t g = key_of(pos0 + key);
+      if constexpr (FMT == FMT_MXFP4)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(A.k_sf + g * 4),
+                                         (__attribute__((address_space(3))) void*)(sl.sf + buf * G::kKeys + wave * kWave),
+                                         4, 0, 0);
+      if (has_ks)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(A.k_scale + g),
+                                         (__attribute__((address_space(3))) void*)(sl.ks + buf * G::kKeys + wave * kWave),
+                                         4, 0, 0);
     }
   };
 
   const int nst = (tB - tA + G::kTiles - 1) / G::kTiles;
-  gload(0);
-  lwrite(0);
+  dma(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int st = 0; st < nst; ++st) {
     const int buf = st & 1;
     const bool more = st + 1 < nst;
-    if (more) gload(st + 1);
+    if (more) dma(st + 1, buf ^ 1);
     const int tbase = tA + st * G::kTiles;
     bool whole = false;  // wave-uniform: every tile of the stage is this wave's and inside all its rows
     if constexpr (!SHARED && RW >= 4)  // (a second copy of the tile loop; 2-row kernels lack the registers)
@@ -685,7 +687,7 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
         if (mine) compute(buf, i, t, false);
       }
     }
-    if (more) lwrite(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next stage
     __syncthreads();
   }
   if constexpr (MODE == MODE_FILTER) {
