@@ -190,7 +190,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long", choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-rows", type=int, default=16, help="rows in the oracle's timed sample (0: skip)")
+    ap.add_argument("--cpu-rows", type=int, default=96, help="rows in the oracle's timed sample (0: skip)")
     ap.add_argument("--routing", action="store_true",
                     help="only measure dense (idx_score + idx_select) against fused top-k over context lengths")
     ap.add_argument("--no-secondary", action="store_true",
