@@ -631,19 +631,29 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
   constexpr int kSlots = G::kKeys * kSlotsPerKey;
   constexpr int kSlotIters = (kSlots + kThreads - 1) / kThreads;
   const bool has_ks = A.k_scale != nullptr;
+  // LDS destination of a stage load, as an address the compiler cannot trace to a variable.
+  auto lds_dst = [](const void* p) -> __attribute__((address_space(3))) void* {
+    uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+    asm volatile("" : "+s"(a));
+    return (__attribute__((address_space(3))) void*)(uintptr_t)a;
+  };
   auto dma = [&](int stage, int buf) {
     const int64_t pos0 = (int64_t)(tA + stage * G::kTiles) * kTile;
     uint8_t* lbase = sl.codes + buf * G::kBytes;
+    int ln = l;
+    // Paged stages: the lane-derived slot offsets are recomputed per stage rather than held
+    // in registers, which the 64-head kernels would otherwise spill.
+    if constexpr (SHARED) asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int u = 0; u < kSlotIters; ++u) {
       const int s0 = u * kThreads + wave * kWave;
       if (s0 < kSlots) {  // wave-uniform
-        const int sidx = s0 + l;
+        const int sidx = s0 + ln;
         const int key = sidx / kSlotsPerKey, part = sidx % kSlotsPerKey;
         const int pp = part < KB / 16 ? part : 0;
         const uint8_t* src = A.k + key_of(pos0 + key) * KB + pp * 16;
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                         (__attribute__((address_space(3))) void*)(lbase + s0 * 16), 16, 0, 0);
+                                         lds_dst(lbase + s0 * 16), 16, 0, 0);
       }
     }
     if (wave * kWave < G::kKeys) {  // wave-uniform
@@ -651,11 +661,11 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
       const int64_t g = key_of(pos0 + key);
       if constexpr (FMT == FMT_MXFP4)
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(A.k_sf + g * 4),
-                                         (__attribute__((address_space(3))) void*)(sl.sf + buf * G::kKeys + wave * kWave),
+                                         lds_dst(sl.sf + buf * G::kKeys + wave * kWave),
                                          4, 0, 0);
       if (has_ks)
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(A.k_scale + g),
-                                         (__attribute__((address_space(3))) void*)(sl.ks + buf * G::kKeys + wave * kWave),
+                                         lds_dst(sl.ks + buf * G::kKeys + wave * kWave),
                                          4, 0, 0);
     }
   };
