@@ -87,7 +87,7 @@ struct TileWork {
   int32_t nrb;     // row blocks
   int32_t nchunk;  // position chunks per row block
   int32_t chunk;   // positions per chunk (multiple of kTile)
-  int32_t pad;
+  int32_t spread;  // 1: every chunk's row blocks are dealt over all XCDs (keys private to a row block)
   int64_t total;   // nrb * nchunk
 };
 
@@ -97,6 +97,10 @@ struct TileWork {
 //    are fetched into that XCD's L2 once and the chunks near the start of the key range,
 //    which short rows still reach, are spread over all XCDs.  Grid: ceil(nchunk / 8) * 8
 //    * nrb workgroups.
+//  - At least 8 chunks and spread (paged keys: a row block's keys are its own, so an XCD
+//    gains nothing from holding whole chunks): item (c, j) runs on XCD (c + j) % 8.  Later
+//    chunks hold less work (fewer rows reach them), and this keeps the XCDs' shares even.
+//    Same grid.
 //  - Fewer chunks: XCD x takes the x-th eighth of the items, so every XCD has work.  Grid:
 //    8 * ceil(total / 8) workgroups.
 __device__ __forceinline__ int64_t map_item(const TileWork& W) {
@@ -104,7 +108,18 @@ __device__ __forceinline__ int64_t map_item(const TileWork& W) {
   const int64_t x = b & 7, local = b >> 3;
   if (W.nchunk < 8) return x * ((W.total + 7) / 8) + local;
   const int64_t g = local / W.nrb, j = local % W.nrb;
-  return (g * 8 + x) * W.nrb + j;
+  if (!W.spread) return (g * 8 + x) * W.nrb + j;
+  // Chunk c of group g gives XCD x its row blocks r0, r0 + 8, ... with r0 = (x - c) mod 8;
+  // over the group's 8 chunks those are nrb items, taken chunk by chunk.
+  int64_t rem = j;
+  for (int i = 0; i < 8; ++i) {
+    const int64_t c = g * 8 + i;
+    const int64_t r0 = (x - c) & 7;
+    const int64_t n = (W.nrb - r0 + 7) >> 3;
+    if (rem < n) return c * W.nrb + r0 + 8 * rem;
+    rem -= n;
+  }
+  return W.total;  // not reached: the group's counts add up to nrb
 }
 
 // ============================================================================= contiguous K
@@ -1080,7 +1095,7 @@ static TileWork tile_work(const DevProblem& P, int64_t positions, int chunk) {
   W.chunk = chunk;
   W.nchunk = (int)((positions + chunk - 1) / chunk);
   if (W.nchunk < 1) W.nchunk = 1;
-  W.pad = 0;
+  W.spread = P.page_table != nullptr;
   W.total = (int64_t)W.nrb * W.nchunk;
   return W;
 }
