@@ -659,6 +659,36 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
     // Paged stages: the lane-derived slot offsets are recomputed per stage rather than held
     // in registers, which the 64-head kernels would otherwise spill.
     if constexpr (SHARED) asm volatile("" : "+v"(ln));
+    if constexpr (MODE != MODE_SAMPLE) {
+      // Paged, page ids in LDS, one position per key: key_of in 32-bit arithmetic.
+      if (req >= 0 && pg_cached) {  // wave-uniform
+        const int kpos0 = (int)pos0, pbase = (int)pg_lo;
+#pragma unroll
+        for (int u = 0; u < kSlotIters; ++u) {
+          const int s0 = u * kThreads + wave * kWave;
+          if (s0 < kSlots) {
+            const int sidx = s0 + ln;
+            const int key = min(kpos0 + sidx / kSlotsPerKey, lmax), part = sidx % kSlotsPerKey;
+            const int32_t id = sl.pages[(key >> 6) - pbase];
+            const int32_t off = (key & (kPage - 1)) * KB + (part < KB / 16 ? part : 0) * 16;
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(A.k + (int64_t)id * (kPage * KB) + off),
+                lds_dst(lbase + s0 * 16), 16, 0, 0);
+          }
+        }
+        if (wave * kWave < G::kKeys) {
+          const int key = min(kpos0 + wave * kWave + ln, lmax);
+          const int64_t g = (int64_t)sl.pages[(key >> 6) - pbase] * kPage + (key & (kPage - 1));
+          if constexpr (FMT == FMT_MXFP4)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(A.k_sf + g * 4),
+                                             lds_dst(sl.sf + buf * G::kKeys + wave * kWave), 4, 0, 0);
+          if (has_ks)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(A.k_scale + g),
+                                             lds_dst(sl.ks + buf * G::kKeys + wave * kWave), 4, 0, 0);
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int u = 0; u < kSlotIters; ++u) {
       const int s0 = u * kThreads + wave * kWave;
