@@ -652,6 +652,7 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
     asm volatile("" : "+s"(a));
     return (__attribute__((address_space(3))) void*)(uintptr_t)a;
   };
+  const bool fits32 = (int64_t)phase + ((int64_t)tB + G::kTiles) * kTile * S < 0x7FFFFFFF;
   auto dma = [&](int stage, int buf) {
     const int64_t pos0 = (int64_t)(tA + stage * G::kTiles) * kTile;
     uint8_t* lbase = sl.codes + buf * G::kBytes;
@@ -659,16 +660,17 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
     // Paged stages: the lane-derived slot offsets are recomputed per stage rather than held
     // in registers, which the 64-head kernels would otherwise spill.
     if constexpr (SHARED) asm volatile("" : "+v"(ln));
-    if constexpr (MODE != MODE_SAMPLE) {
-      // Paged, page ids in LDS, one position per key: key_of in 32-bit arithmetic.
-      if (req >= 0 && pg_cached) {  // wave-uniform
+    {
+      // Paged with the page ids in LDS: key_of in 32-bit arithmetic when every position the
+      // stages reach, times the stride, stays below 2^31.
+      if (req >= 0 && pg_cached && fits32) {  // wave-uniform
         const int kpos0 = (int)pos0, pbase = (int)pg_lo;
 #pragma unroll
         for (int u = 0; u < kSlotIters; ++u) {
           const int s0 = u * kThreads + wave * kWave;
           if (s0 < kSlots) {
             const int sidx = s0 + ln;
-            const int key = min(kpos0 + sidx / kSlotsPerKey, lmax), part = sidx % kSlotsPerKey;
+            const int key = min(phase + (kpos0 + sidx / kSlotsPerKey) * S, lmax), part = sidx % kSlotsPerKey;
             const int32_t id = sl.pages[(key >> 6) - pbase];
             const int32_t off = (key & (kPage - 1)) * KB + (part < KB / 16 ? part : 0) * 16;
             __builtin_amdgcn_global_load_lds(
@@ -677,7 +679,7 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
           }
         }
         if (wave * kWave < G::kKeys) {
-          const int key = min(kpos0 + wave * kWave + ln, lmax);
+          const int key = min(phase + (kpos0 + wave * kWave + ln) * S, lmax);
           const int64_t g = (int64_t)sl.pages[(key >> 6) - pbase] * kPage + (key & (kPage - 1));
           if constexpr (FMT == FMT_MXFP4)
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(A.k_sf + g * 4),
