@@ -1173,6 +1173,7 @@ static hipError_t dispatch_score(const DevProblem& P, const LinArgs& L, const Ep
 
 // Keys per work item of the score kernels: long enough to amortise a workgroup's row
 // operand loads (up to 16384), short enough that the grid keeps about 8192 workgroups.
+constexpr int64_t kSampleItems = 1024;
 static int chunk_keys(const DevProblem& P) {
   const int rb = rows_per_block_for(P);
   const int64_t nrb = (P.rows + rb - 1) / rb;
@@ -1180,7 +1181,18 @@ static int chunk_keys(const DevProblem& P) {
   c = (c + 4095) / 4096 * 4096;
   return (int)std::min<int64_t>(std::max<int64_t>(c, 4096), 16384);
 }
-constexpr int kChunkSamples = 2048;
+// Sample slots per work item of the sample pass: 2048 (the LDS page cache covers that many at
+// the largest stride).  Paged keys, whose row blocks are few and read keys of their own, take
+// fewer, so that the pass has about 1024 work items to spread over the CUs; contiguous keys
+// gain nothing from that (each item reloads its rows' operands).
+static int chunk_samples(const DevProblem& P, int32_t ns) {
+  if (P.page_table == nullptr) return 2048;
+  const int rb = rows_per_block_for(P);
+  const int64_t nrb = (P.rows + rb - 1) / rb;
+  int64_t c = ((int64_t)std::max(ns, 1) * nrb + kSampleItems - 1) / kSampleItems;
+  c = (c + 127) / 128 * 128;
+  return (int)std::min<int64_t>(std::max<int64_t>(c, 256), 2048);
+}
 
 size_t lin_ws_bytes(int32_t rows) {
   return (size_t)rows * kLinRowBytes + (((size_t)rows * kLinRowScales + 255) & ~(size_t)255) + 256;
@@ -1220,7 +1232,7 @@ hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_id
     E.stride = F.stride;
     E.skip_le = F.cap;
     if (F.debug_mode != 0 && F.debug_row_mod <= 0) E.skip_le = 0x7FFFFFFF;  // every row forced
-    if ((e = dispatch_score<MODE_SAMPLE>(P, L, E, tile_work(P, F.ns, kChunkSamples), s)) != hipSuccess)
+    if ((e = dispatch_score<MODE_SAMPLE>(P, L, E, tile_work(P, F.ns, chunk_samples(P, F.ns)), s)) != hipSuccess)
       return e;
     if ((e = mark(1)) != hipSuccess) return e;
   }
