@@ -278,8 +278,10 @@ __device__ __forceinline__ void mfma_row(v16f (&acc)[H / 32], const RowOperand<F
 #pragma unroll
   for (int mt = 0; mt < H / 32; ++mt) {
     v16f a = {};
-    a = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ro.a[mt][0], ko.b[0], a, C, C, 0, ro.sa[mt][0], 0, ko.sb[0]);
-    a = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ro.a[mt][1], ko.b[1], a, C, C, 0, ro.sa[mt][1], 0, ko.sb[1]);
+    // Scale operands carry both K-steps: the byte select picks K-step ks (byte ks of the
+    // query word, byte 2 ks of the key word).
+    a = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ro.a[mt][0], ko.b[0], a, C, C, 0, ro.sa[mt], 0, ko.sb);
+    a = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ro.a[mt][1], ko.b[1], a, C, C, 1, ro.sa[mt], 2, ko.sb);
     acc[mt] = a;
   }
 }
@@ -290,7 +292,7 @@ __device__ __forceinline__ void mfma_row(v16f (&acc)[H / 32], const RowOperand<F
 // piece dot products of row row0 + 2 (s / 5) + H, the row its head sums land on.
 struct LinOperand {
   v8i a[2];
-  int sa[2];
+  int sa;  // block scales of the two K-steps, byte ks
 };
 
 __device__ __forceinline__ void load_lin(LinOperand& lo, const LinArgs& L, int row0, int rows, int npairs) {
@@ -307,11 +309,15 @@ __device__ __forceinline__ void load_lin(LinOperand& lo, const LinArgs& L, int r
       const v4i x0 = *reinterpret_cast<const v4i*>(L.q8 + base * 32);
       const int2 x1 = *reinterpret_cast<const int2*>(L.q8 + base * 32 + 16);
       lo.a[ks] = v8i{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, 0, 0};
-      lo.sa[ks] = L.sf[base];
     } else {
       lo.a[ks] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-      lo.sa[ks] = 127;
     }
+  }
+  if (ok) {
+    const int64_t b0 = (((int64_t)row * kPieces + c) * 2) * 2 + half;  // K-step 0; K-step 1 is b0 + 2
+    lo.sa = (int)L.sf[b0] | ((int)L.sf[b0 + 2] << 8);
+  } else {
+    lo.sa = 0x7F7F;
   }
 }
 
@@ -319,8 +325,8 @@ template <int FMT>
 __device__ __forceinline__ v16f mfma_lin(const LinOperand& lo, const KeyOperand& ko) {
   constexpr int C = Fmt<FMT>::kCode;
   v16f a = {};
-  a = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(lo.a[0], ko.b[0], a, 2, C, 0, lo.sa[0], 0, ko.sb[0]);
-  a = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(lo.a[1], ko.b[1], a, 2, C, 0, lo.sa[1], 0, ko.sb[1]);
+  a = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(lo.a[0], ko.b[0], a, 2, C, 0, lo.sa, 0, ko.sb);
+  a = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(lo.a[1], ko.b[1], a, 2, C, 1, lo.sa, 2, ko.sb);
   return a;
 }
 
@@ -430,18 +436,21 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
   load_lin(lo, L, row0, A.rows, NP);
 
   float thr_l[NP];
-  int ks_l[NP], lo_l[NP], hi_l[NP];
-  int64_t row_l[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int i = 2 * p + half;
-    row_l[p] = row0 + i;
-    ks_l[p] = half ? ksr[2 * p + 1] : ksr[2 * p];
-    lo_l[p] = half ? plo[2 * p + 1] : plo[2 * p];
-    hi_l[p] = half ? phi[2 * p + 1] : phi[2 * p];
     thr_l[p] = 0.0f;
     if (MODE == MODE_FILTER && row0 + i < A.rows) thr_l[p] = E.thr[row0 + i];
   }
+  // Per-lane value of pair p (row 2p on lanes 0-31, row 2p + 1 on lanes 32-63), formed where
+  // it is used from the wave-uniform per-row values, so that it holds no VGPR across the
+  // tile loop (the empty asm keeps the select from being hoisted out of the loop).
+  auto lane_pair = [&](const int (&v)[RW], int p) -> int {
+    int a = v[2 * p], b = v[2 * p + 1];
+    asm volatile("" : "+v"(a), "+v"(b));
+    return half ? b : a;
+  };
+  auto row_of = [&](int p) -> int64_t { return (int64_t)row0 + 2 * p + half; };
   const int64_t last_key = A.num_keys - 1;
   // Physical key of stage position pos: contiguous keys are clamped to the key array;
   // paged keys (all rows of request `req`) are clamped to the rows' visible range, then
@@ -528,7 +537,7 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
       } else {
 #pragma unroll
         for (int p = 0; p < NP; ++p)
-          m[p] = wave_ballot(pos >= lo_l[p] && pos < hi_l[p] && score_of[p] >= thr_l[p]);
+          m[p] = wave_ballot(pos >= lane_pair(plo, p) && pos < lane_pair(phi, p) && score_of[p] >= thr_l[p]);
       }
 #pragma unroll
       for (int p = 0; p < NP; ++p) any |= m[p];
@@ -541,7 +550,7 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
             const int slot = (half ? ccnt[2 * p + 1] - nA : ccnt[2 * p]) + mask_prefix(m[p]);
             const int o = (2 * p + half) * kCandBuf + slot;
             cs[o] = score_of[p];
-            ci[o] = (int32_t)(key - ks_l[p]);
+            ci[o] = (int32_t)(key - lane_pair(ksr, p));
           }
           ccnt[2 * p] += nA;
           ccnt[2 * p + 1] += nB;
@@ -554,13 +563,13 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         const float score = score_of[p];
-        const bool valid = full || (pos >= lo_l[p] && pos < hi_l[p]);
+        const bool valid = full || (pos >= lane_pair(plo, p) && pos < lane_pair(phi, p));
         if constexpr (MODE == MODE_STORE) {
-          if (valid) E.out[row_l[p] * E.ld + (key - ks_l[p])] = score;
+          if (valid) E.out[row_of(p) * E.ld + (key - lane_pair(ksr, p))] = score;
         } else if constexpr (MODE == MODE_ROWSTORE) {
-          if (valid && row_l[p] == E.only_row) E.out[key - ks_l[p]] = score;
+          if (valid && row_of(p) == E.only_row) E.out[key - lane_pair(ksr, p)] = score;
         } else {
-          if (valid) E.samp[row_l[p] * E.ns + pos] = score;
+          if (valid) E.samp[row_of(p) * E.ns + pos] = score;
         }
       }
     }
@@ -568,27 +577,50 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
 
 
   // Key operand and half key scale of tile slot i of LDS stage buffer `buf`.
-  auto read_b = [&](int buf, int i, KeyOperand& ko, float& half_kscale) {
-    const int kidx = i * kTile + col;
-    const uint8_t* row = sl.codes + buf * G::kBytes + kidx * G::kStride;
+  // This lane's LDS addresses in stage buffer `buf` (codes of key `col` at this lane
+  // half's K offset, its block-scale word and key scale), made opaque to the compiler so
+  // that each tile's reads use the tile's constant offset from them instead of a register
+  // per tile.
+  typedef const __attribute__((address_space(3))) uint8_t* lds_ptr;
+  struct StageBase {
+    lds_ptr codes, sf, ks;
+  };
+  auto stage_base = [&](int buf) -> StageBase {
+    auto opaque = [](const void* p) -> lds_ptr {
+      uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+      asm volatile("" : "+v"(a));
+      return (lds_ptr)(uintptr_t)a;
+    };
+    constexpr int kHalfOff = FMT == FMT_E4M3 ? 32 : 16;
+    return StageBase{opaque(sl.codes + buf * G::kBytes + col * G::kStride + half * kHalfOff),
+                     opaque(sl.sf + buf * G::kKeys + col), opaque(sl.ks + buf * G::kKeys + col)};
+  };
+  // Key operand and half key scale of tile slot i of the stage at `sb`.
+  auto read_b = [&](const StageBase& sb, int i, KeyOperand& ko, float& half_kscale) {
+    lds_ptr row = sb.codes + i * kTile * G::kStride;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       if constexpr (FMT == FMT_E4M3) {
-        const v4i x0 = *reinterpret_cast<const v4i*>(row + ks * 64 + half * 32);
-        const v4i x1 = *reinterpret_cast<const v4i*>(row + ks * 64 + half * 32 + 16);
+        const v4i x0 = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(row + ks * 64);
+        const v4i x1 = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(row + ks * 64 + 16);
         ko.b[ks] = v8i{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        ko.sb[ks] = 127;
       } else {
-        const v4i x = *reinterpret_cast<const v4i*>(row + ks * 32 + half * 16);
+        const v4i x = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(row + ks * 32);
         ko.b[ks] = v8i{x.x, x.y, x.z, x.w, 0, 0, 0, 0};
       }
     }
     if constexpr (FMT == FMT_MXFP4) {
-      const uint32_t sw = sl.sf[buf * G::kKeys + kidx];
-      ko.sb[0] = (sw >> (8 * half)) & 0xFF;
-      ko.sb[1] = (sw >> (8 * (2 + half))) & 0xFF;
+      // The key's four block scales, shifted so that bytes 0 and 2 hold this lane half's
+      // blocks of K-steps 0 and 1.
+      const uint32_t sw = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(sb.sf + i * kTile * 4);
+      ko.sb = (int)(sw >> (8 * half));
+    } else {
+      ko.sb = 0x7F7F7F7F;
     }
-    half_kscale = A.k_scale ? 0.5f * sl.ks[buf * G::kKeys + kidx] : 0.5f;
+    // Read unconditionally and select (no branch per tile); without key scales the LDS
+    // word is never written and its value is discarded.
+    const float kv = *reinterpret_cast<const __attribute__((address_space(3))) float*>(sb.ks + i * kTile * 4);
+    half_kscale = A.k_scale ? 0.5f * kv : 0.5f;
   };
   struct Acc {
     v16f row[RW][H / 32];
@@ -627,10 +659,10 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
       sc[p] = finish_score2(combine_halves(part[2 * p], part[2 * p + 1]), lin_of_pair(a.lin, p), half_kscale);
   };
   // One tile: key operand from LDS, MFMAs for all RW rows and the linear tile, reduce, epilogue.
-  auto compute = [&](int buf, int i, int t, bool known_full) {
+  auto compute = [&](const StageBase& sb, int i, int t, bool known_full) {
     KeyOperand ko;
     float ksc;
-    read_b(buf, i, ko, ksc);
+    read_b(sb, i, ko, ksc);
     Acc a;
     issue(a, ko);
     float sc[NP];
@@ -726,14 +758,29 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
     const bool more = st + 1 < nst;
     if (more) dma(st + 1, buf ^ 1);
     const int tbase = tA + st * G::kTiles;
+    const StageBase sbase = stage_base(buf);
     bool whole = false;  // wave-uniform: every tile of the stage is this wave's and inside all its rows
     if constexpr (!SHARED && RW >= 4)  // (a second copy of the tile loop; 2-row kernels lack the registers)
       whole = tbase >= wt0 && tbase + G::kTiles <= min(wt1, tB) && tbase * kTile >= full_lo &&
               (tbase + G::kTiles) * kTile <= full_hi;
     if (whole) {
       if constexpr (!SHARED && RW >= 4) {
+        // The next tile's key operand is read from LDS once this tile's MFMAs are issued
+        // (into the registers they have just read), so the LDS latency runs under this
+        // tile's head reduce instead of stalling the next tile's MFMAs.
+        KeyOperand ko;
+        float ksc;
+        read_b(sbase, 0, ko, ksc);
 #pragma unroll
-        for (int i = 0; i < G::kTiles; ++i) compute(buf, i, tbase + i, true);
+        for (int i = 0; i < G::kTiles; ++i) {
+          Acc a;
+          issue(a, ko);
+          const float ksc_i = ksc;
+          if (i + 1 < G::kTiles) read_b(sbase, i + 1, ko, ksc);
+          float sc[NP];
+          reduce(a, ksc_i, sc);
+          epilogue(tbase + i, sc, true);
+        }
       }
     } else {
 #pragma unroll
@@ -741,7 +788,7 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
         const int t = tbase + i;
         if (t >= tB) break;  // workgroup-uniform
         const bool mine = SHARED ? ((i % split) == (slot < 0 ? wave : slot)) : (t >= wt0 && t < wt1);
-        if (mine) compute(buf, i, t, false);
+        if (mine) compute(sbase, i, t, false);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next stage

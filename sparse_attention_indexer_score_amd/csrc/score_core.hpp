@@ -60,7 +60,7 @@ template <int FMT, int H>
 struct RowOperand {
   static constexpr int MT = H / 32;
   v8i a[MT][2];
-  int sa[MT][2];
+  int sa[MT];  // e8m0 block scales of the two K-steps, byte ks (the MFMA's scale byte select)
   float w[MT][16];
 };
 
@@ -80,12 +80,15 @@ __device__ __forceinline__ void load_row(RowOperand<FMT, H>& ro, const ScoreArgs
         const v4i* src = reinterpret_cast<const v4i*>(qp + ks * 64 + half * 32);
         const v4i x0 = src[0], x1 = src[1];
         ro.a[mt][ks] = v8i{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        ro.sa[mt][ks] = 127;
       } else {
         const v4i x = *reinterpret_cast<const v4i*>(qp + ks * 32 + half * 16);
         ro.a[mt][ks] = v8i{x.x, x.y, x.z, x.w, 0, 0, 0, 0};
-        ro.sa[mt][ks] = A.q_sf[hv * 4 + ks * 2 + half];
       }
+    }
+    if constexpr (FMT == FMT_E4M3) {
+      ro.sa[mt] = 0x7F7F;  // 1.0 for both K-steps
+    } else {
+      ro.sa[mt] = (int)A.q_sf[hv * 4 + half] | ((int)A.q_sf[hv * 4 + 2 + half] << 8);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -98,7 +101,7 @@ __device__ __forceinline__ void load_row(RowOperand<FMT, H>& ro, const ScoreArgs
 // Key-side operand of one key per lane (lane l supplies key l % 32 of the block).
 struct KeyOperand {
   v8i b[2];
-  int sb[2];
+  int sb;  // e8m0 block scales: byte 0 for K-step 0, byte 2 for K-step 1
 };
 
 // Add the two half-wave partials of row A (pa) and row B (pb): lanes 0-31 receive the
