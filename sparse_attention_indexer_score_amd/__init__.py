@@ -215,14 +215,16 @@ def idx_row_split(rows: int, row_len: int, cu_count: int) -> int:
 
 
 def idx_select(scores: torch.Tensor, length: torch.Tensor, k: int, row_start: Optional[torch.Tensor] = None,
-               out: Optional[torch.Tensor] = None, split: Optional[int] = None, stream=None) -> torch.Tensor:
-    """Exact top-k of each row of scores[rows, ld] (row r: scores[r, row_start[r] + j], j < length[r])."""
+               out: Optional[torch.Tensor] = None, split: Optional[int] = None, stream=None,
+               workspace: bool = True) -> torch.Tensor:
+    """Exact top-k of each row of scores[rows, ld] (row r: scores[r, row_start[r] + j], j < length[r]).
+    workspace=False passes no workspace (the row split is then off: one workgroup per row)."""
     assert scores.dtype == torch.float32 and scores.dim() == 2 and scores.is_contiguous()
     rows, ld = scores.shape
     if out is None:
         out = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
-    nb = idx_select_workspace(rows, ld, k)
-    ws = _workspace(nb, scores.device)
+    nb = idx_select_workspace(rows, ld, k) if workspace else 0
+    ws = _workspace(nb, scores.device) if workspace else None
     L = _lib()
     if split is None:
         rc = L.idx_select(_ptr(scores), ld, _ptr(row_start), _ptr(length), rows, k, _ptr(out), _ptr(ws), nb,

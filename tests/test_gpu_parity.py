@@ -219,11 +219,13 @@ def _sample_positions(n, seg=64, nseg=64):
     return np.concatenate([np.arange(a, a + seg) for a in starts])
 
 
-def test_select_sampled_threshold_misjudged():
+@pytest.mark.parametrize("workspace", [True, False])
+def test_select_sampled_threshold_misjudged(workspace):
     """Rows built so the sampled threshold misjudges them: too few candidates (the sample
     holds the only large values), too many (the sample holds the only small ones), a
     sample that lands exactly on the k-th value, and a short row below the buffer size.
-    Every case must still equal the oracle (the exact fallback takes over)."""
+    Every case must still equal the oracle (the exact fallback takes over), with and
+    without a workspace passed through the C ABI."""
     rng = np.random.default_rng(21)
     ld, k = 65536, 2048
     x = rng.uniform(0.0, 0.5, size=(5, ld)).astype(np.float32)
@@ -235,16 +237,19 @@ def test_select_sampled_threshold_misjudged():
     x[3, pos] = np.float32(0.75)                                                 # 4096 equal sample values
     n = np.array([ld, ld, ld, ld, 6000], dtype=np.int32)
     ref = oracle.select_rows(x, n, k)
-    got = sai.idx_select(torch.from_numpy(x).cuda(), torch.from_numpy(n).cuda(), k, split=0).cpu().numpy()
-    assert_same_sets(got, ref, "sampled select")
+    got = sai.idx_select(torch.from_numpy(x).cuda(), torch.from_numpy(n).cuda(), k, split=0,
+                         workspace=workspace).cpu().numpy()
+    assert_same_sets(got, ref, f"sampled select (workspace={workspace})")
 
 
-def test_select_short_and_empty_rows():
+@pytest.mark.parametrize("workspace", [True, False])
+def test_select_short_and_empty_rows(workspace):
     rng = np.random.default_rng(3)
     x = rng.standard_normal((5, 300)).astype(np.float32)
     n = np.array([0, 1, 10, 299, 300], dtype=np.int32)
     ref = oracle.select_rows(x, n, 64)
-    got = sai.idx_select(torch.from_numpy(x).cuda(), torch.from_numpy(n).cuda(), 64).cpu().numpy()
+    got = sai.idx_select(torch.from_numpy(x).cuda(), torch.from_numpy(n).cuda(), 64,
+                         workspace=workspace).cpu().numpy()
     assert_same_sets(got, ref)
 
 
