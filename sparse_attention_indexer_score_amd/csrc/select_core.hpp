@@ -420,6 +420,22 @@ __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out,
   static_assert(SM::kCap >= kSelSamples, "the sample lives in the candidate buffer");
   constexpr int SEG = 64, NSEG = kSelSamples / SEG;  // 32 runs of 64 consecutive keys
   const int l = lane_id();
+  // Streaming pass state: 16-byte loads, UV per thread per step, the next step's loads
+  // issued before this step's keys are tested.  The first step's loads do not depend on
+  // the threshold, so they are issued before the sample is taken and arrive under it.
+  constexpr int UV = 4;
+  const bool vec = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+  const float4* xv = reinterpret_cast<const float4*>(x);
+  const int nv = vec ? n / 4 : 0;
+  float4 cur[UV], nxt[UV];
+  auto load = [&](float4* v, int base) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < UV; ++u) {
+      const int jv = base + u * NT + (int)threadIdx.x;
+      v[u] = jv < nv ? xv[jv] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  if (nv > 0) load(cur, 0);
   uint32_t T = 0;
   if (threadIdx.x == 0) {
     sm.kmin = 0xFFFFFFFFu;
@@ -458,8 +474,8 @@ __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out,
   }
   __syncthreads();
   uint32_t kmax = 0u;
-  // Appends the lanes' keys k_[u] (element j0 + u * ustride) that pass, one LDS atomic per wave.
-  auto append = [&](const uint32_t* k_, const bool* ok, int j0, int ustride, auto Uc) __attribute__((always_inline)) {
+  // Appends the lanes' keys k_[u] (element ix_[u]) that pass, one LDS atomic per wave.
+  auto append = [&](const uint32_t* k_, const bool* ok, const int* ix_, auto Uc) __attribute__((always_inline)) {
     constexpr int U = decltype(Uc)::value;
     uint64_t mk[U];
     int tot = 0;
@@ -478,7 +494,7 @@ __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out,
           const int slot = at + mask_prefix(mk[u]);
           if (slot < SM::kCap) {
             sm.tkey[slot] = k_[u];
-            sm.tidx[slot] = j0 + u * ustride;
+            sm.tidx[slot] = ix_[u];
           }
           kmax = max(kmax, k_[u]);
         }
@@ -486,47 +502,43 @@ __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out,
       }
     }
   };
-  int done = 0;  // elements [0, done) handled by the vector loop
-  if ((reinterpret_cast<uintptr_t>(x) & 15) == 0) {
-    // 16-byte loads, UV per thread per step, the next step's loads issued before this
-    // step's keys are tested.
-    constexpr int UV = 4;
-    const float4* xv = reinterpret_cast<const float4*>(x);
-    const int nv = n / 4;
-    float4 cur[UV], nxt[UV];
-    auto load = [&](float4* v, int base) __attribute__((always_inline)) {
+  // Vector part: one append (one LDS atomic per wave) for all 4 * UV keys of a step.
+  for (int base = 0; base < nv; base += UV * NT) {
+    if (base + UV * NT < nv) load(nxt, base + UV * NT);
+    uint32_t k_[4 * UV];
+    bool ok[4 * UV];
+    int ix_[4 * UV];
 #pragma unroll
-      for (int u = 0; u < UV; ++u) {
-        const int jv = base + u * NT + (int)threadIdx.x;
-        v[u] = jv < nv ? xv[jv] : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int u = 0; u < UV; ++u) {
+      const int jv = base + u * NT + (int)threadIdx.x;
+      k_[4 * u + 0] = order_key(cur[u].x);
+      k_[4 * u + 1] = order_key(cur[u].y);
+      k_[4 * u + 2] = order_key(cur[u].z);
+      k_[4 * u + 3] = order_key(cur[u].w);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        ok[4 * u + c] = jv < nv;
+        ix_[4 * u + c] = 4 * jv + c;
       }
-    };
-    if (nv > 0) load(cur, 0);
-    for (int base = 0; base < nv; base += UV * NT) {
-      if (base + UV * NT < nv) load(nxt, base + UV * NT);
-#pragma unroll
-      for (int u = 0; u < UV; ++u) {
-        const int jv = base + u * NT + (int)threadIdx.x;
-        const uint32_t k_[4] = {order_key(cur[u].x), order_key(cur[u].y), order_key(cur[u].z), order_key(cur[u].w)};
-        const bool ok[4] = {jv < nv, jv < nv, jv < nv, jv < nv};
-        append(k_, ok, 4 * jv, 1, std::integral_constant<int, 4>{});
-      }
-#pragma unroll
-      for (int u = 0; u < UV; ++u) cur[u] = nxt[u];
     }
-    done = nv * 4;
+    append(k_, ok, ix_, std::integral_constant<int, 4 * UV>{});
+#pragma unroll
+    for (int u = 0; u < UV; ++u) cur[u] = nxt[u];
   }
+  // Scalar part: the rest (all of the row when it is not 16-byte aligned).
   constexpr int U = 8;
-  for (int base = done; base < n; base += U * NT) {
+  for (int base = nv * 4; base < n; base += U * NT) {
     uint32_t k_[U];
     bool ok[U];
+    int ix_[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = base + u * NT + (int)threadIdx.x;
       ok[u] = j < n;
       k_[u] = ok[u] ? order_key(x[j]) : 0u;
+      ix_[u] = j;
     }
-    append(k_, ok, base + (int)threadIdx.x, NT, std::integral_constant<int, U>{});
+    append(k_, ok, ix_, std::integral_constant<int, U>{});
   }
   kmax = wave_max_u32(kmax);
   if (l == 0 && kmax) atomicMax(&sm.kmax, kmax);
