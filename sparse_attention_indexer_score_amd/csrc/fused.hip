@@ -943,8 +943,25 @@ struct ThrArgs {
   int32_t debug_mode, debug_row_mod;
 };
 
-__global__ __launch_bounds__(kThreads) void threshold_kernel(ThrArgs T) {
+// Two shapes of the threshold kernel.  Rows with many samples (long contexts): 1024-thread
+// workgroups that hold up to 15360 sample keys in LDS (60 KB; with the histogram two
+// workgroups fit on a CU), so the samples are read from memory once instead of once per
+// pass.  Rows with few samples: 256-thread workgroups without the LDS copy, many per CU.
+// Rows with more samples than the LDS copy holds read them from global memory on every pass.
+template <int NT, int STAGE>
+struct ThrStage {
+  uint32_t key[STAGE];
+};
+template <int NT>
+struct ThrStage<NT, 0> {
+  uint32_t key[1];
+};
+
+template <int kThrThreads, int kThrStage>
+__global__ __launch_bounds__(kThrThreads) void threshold_kernel(ThrArgs T) {
   __shared__ SelSmemT<64> sm;  // histogram and scan scratch only
+  __shared__ ThrStage<kThrThreads, kThrStage> stage;
+  uint32_t* skey = stage.key;
   const int r = blockIdx.x;
   if (r == 0 && threadIdx.x < kStatSlots) T.stats[threadIdx.x] = (threadIdx.x == kStatMin) ? 0x7FFFFFFF : 0;
   if (r == 0 && threadIdx.x < 2) T.fb_ctrl[threadIdx.x] = 0;
@@ -979,14 +996,20 @@ __global__ __launch_bounds__(kThreads) void threshold_kernel(ThrArgs T) {
         sm.kmin = 0xFFFFFFFFu;
         sm.kmax = 0u;
       }
-      zero_hist<kThreads>(sm, kHistBins);
+      zero_hist<kThrThreads>(sm, kHistBins);
       __syncthreads();
+      // The min/max pass reads the samples once; when they fit, their order keys stay in
+      // LDS for the two histogram passes.
+      const bool staged = n <= kThrStage;  // workgroup-uniform (never for kThrStage == 0)
       uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-      for (int j = threadIdx.x; j < n; j += kThreads) {
+#pragma unroll 4
+      for (int j = threadIdx.x; j < n; j += kThrThreads) {
         const uint32_t k = order_key(sp[j]);
+        if (staged) skey[j] = k;
         lo = min(lo, k);
         hi = max(hi, k);
       }
+      auto key_at = [&](int j) -> uint32_t { return staged ? skey[j] : order_key(sp[j]); };
       lo = wave_min_u32(lo);
       hi = wave_max_u32(hi);
       if (lane_id() == 0) {
@@ -995,21 +1018,21 @@ __global__ __launch_bounds__(kThreads) void threshold_kernel(ThrArgs T) {
       }
       __syncthreads();
       const KeyNorm nz = key_norm(sm.kmin, sm.kmax);
-      for (int j = threadIdx.x; j < n; j += kThreads)
-        atomicAdd(&sm.hist[nz.normalize(order_key(sp[j])) >> (32 - kHistBits)], 1u);
+      for (int j = threadIdx.x; j < n; j += kThrThreads)
+        atomicAdd(&sm.hist[nz.normalize(key_at(j)) >> (32 - kHistBits)], 1u);
       __syncthreads();
-      find_boundary<kThreads>(sm, kHistBins, (uint32_t)m);
+      find_boundary<kThrThreads>(sm, kHistBins, (uint32_t)m);
       const uint32_t b1 = (uint32_t)sm.bnd_bin;
       const uint32_t m2 = (uint32_t)m - sm.bnd_above;
       __syncthreads();
-      zero_hist<kThreads>(sm, kHistBins);
+      zero_hist<kThrThreads>(sm, kHistBins);
       __syncthreads();
-      for (int j = threadIdx.x; j < n; j += kThreads) {
-        const uint32_t v = nz.normalize(order_key(sp[j]));
+      for (int j = threadIdx.x; j < n; j += kThrThreads) {
+        const uint32_t v = nz.normalize(key_at(j));
         if ((v >> (32 - kHistBits)) == b1) atomicAdd(&sm.hist[(v >> (32 - 2 * kHistBits)) & (kHistBins - 1)], 1u);
       }
       __syncthreads();
-      find_boundary<kThreads>(sm, kHistBins, m2);
+      find_boundary<kThrThreads>(sm, kHistBins, m2);
       const uint32_t v = (b1 << (32 - kHistBits)) | ((uint32_t)sm.bnd_bin << (32 - 2 * kHistBits));
       tr = order_key_to_float(nz.denormalize(v));
     }
@@ -1301,7 +1324,10 @@ hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_id
     T.rb_rows = rows_per_block_for(P);
     T.debug_mode = F.debug_mode;
     T.debug_row_mod = F.debug_row_mod;
-    threshold_kernel<<<dim3(P.rows), dim3(kThreads), 0, s>>>(T);
+    if (F.ns >= 2048)
+      threshold_kernel<1024, 15360><<<dim3(P.rows), dim3(1024), 0, s>>>(T);
+    else
+      threshold_kernel<kThreads, 0><<<dim3(P.rows), dim3(kThreads), 0, s>>>(T);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(2)) != hipSuccess) return e;
   }
