@@ -1256,7 +1256,16 @@ static int chunk_keys(const DevProblem& P) {
 // fewer, so that the pass has about 1024 work items to spread over the CUs; contiguous keys
 // gain nothing from that (each item reloads its rows' operands).
 static int chunk_samples(const DevProblem& P, int32_t ns) {
-  if (P.page_table == nullptr) return 2048;
+  if (P.page_table == nullptr) {
+    // Contiguous keys: chunks of up to 2048 samples.  When there are at least 8, their
+    // count is a multiple of 8 and they are of equal size (a multiple of the tile), so the
+    // chunks dealt to the 8 XCDs (chunk c on XCD c % 8) hold the same work.
+    if (ns <= 4 * 2048) return 2048;
+    const int64_t n = ((int64_t)ns + 2047) / 2048;
+    const int64_t nc = (n + 7) / 8 * 8;
+    const int64_t c = (((int64_t)ns + nc - 1) / nc + kTile - 1) / kTile * kTile;
+    return (int)c;
+  }
   const int rb = rows_per_block_for(P);
   const int64_t nrb = (P.rows + rb - 1) / rb;
   int64_t c = ((int64_t)std::max(ns, 1) * nrb + kSampleItems - 1) / kSampleItems;
