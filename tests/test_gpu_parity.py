@@ -185,6 +185,17 @@ def test_paged_row_pairs_straddling_requests():
 
 # ----------------------------------------------------------------------------- edges
 
+@pytest.mark.parametrize("k", [1, 7, 100, 1000, 2048])
+def test_fused_k_range_ragged_mxfp4(k):
+    """k from 1 to the maximum on MXFP4 keys with a ragged shape: 21 rows (one full 16-row
+    block and a partial one), 9001 keys (a partial last tile), rows starting at different
+    keys.  Small k gives odd sample strides down to 1; k = 2048 keeps most rows whole."""
+    p = wl.long_context(rows=21, num_keys=9001, band_keys=1000, seed=40 + k)
+    p.ks = np.minimum((np.arange(p.rows, dtype=np.int32) * 37) % 500, p.ke).astype(np.int32)
+    st = full_check(p, k, score_rows=range(0, p.rows, 4))
+    assert st["rows_sampled"] + st["rows_store_all"] == p.rows
+
+
 def test_edge_lengths_e4m3():
     """Empty rows, V < k, V == k, V == cap, V == cap + 1 and full rows; k = 512, cap = 2048."""
     p = wl.tiny(rows=12, num_keys=4096, topk=512, seed=5)
