@@ -26,6 +26,10 @@ What it computes, and where that is defined
   min(k, visible) indices relative to the row's first visible key, pad with -1.
 * Paged K (LiteTopK page, section 3, topk_page_table_transform): logical position s of
   a request lives in physical slot page_table[req][s // 64] * 64 + s % 64.
+* The consumer of the selection, sparse attention of each query row over its selected KV
+  slots (QSA sparse paged attention page, vllm-project/vllm#66512): softmax of the scaled
+  q . k over the selected slots, weights applied to the slots' value vectors
+  (``sparse_attention``).
 
 Readings where the pages are silent:
 * e4m3 is OCP E4M3FN (bias 7, no infinities, 0x7F/0xFF NaN); MXFP4 is OCP e2m1 with
@@ -246,3 +250,46 @@ def page_transform(idx: np.ndarray, page_row: np.ndarray) -> np.ndarray:
     idx = np.asarray(idx, dtype=np.int64)
     out = np.where(idx >= 0, page_row[np.maximum(idx, 0) // PAGE].astype(np.int64) * PAGE + idx % PAGE, -1)
     return out.astype(np.int32)
+
+
+# ------------------------------------------------------------ sparse attention (consumer)
+
+def sparse_attention(q_bits: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, slots: np.ndarray,
+                     softmax_scale: float, output_scale: float) -> np.ndarray:
+    """Attention of each query row over only the KV slots its indexer selected (the consumer
+    of the top-k: QSA sparse paged attention page, vllm-project/vllm#66512, introduction
+    and section 2: every query row attends to about 2048 tokens chosen by the indexer; the
+    logical -> physical slot translation is a separate pass, so this takes physical slots).
+
+    q_bits  uint16 bf16 [rows, hq, 128]
+    k_cache, v_cache  uint8 e4m3 [num_slots, hkv, 128] (one vector per slot and KV head)
+    slots   int32 [rows, width]: physical slots; entries outside [0, num_slots) (e.g. the
+            -1 padding of a short selection) take no part
+    Query head h reads KV head h // (hq // hkv) (grouped query heads share a KV head).
+
+        s_j      = softmax_scale * q[r, h] . k[slot_j, g]
+        out[r,h] = output_scale * sum_j exp(s_j - max s) v[slot_j, g] / sum_j exp(s_j - max s)
+
+    over the valid j; a row with no valid slot gives 0.  Computed in float64 from exactly
+    decoded inputs (bf16 and e4m3 values are exact in float64), returned as float64."""
+    q = decode_bf16(q_bits)
+    kd = decode_e4m3(k_cache)
+    vd = decode_e4m3(v_cache)
+    _check_finite(q, "q")
+    _check_finite(kd, "k_cache")
+    _check_finite(vd, "v_cache")
+    rows, hq, d = q.shape
+    num_slots, hkv, _ = kd.shape
+    group = hq // hkv
+    out = np.zeros((rows, hq, d), dtype=np.float64)
+    for r in range(rows):
+        sl = np.asarray(slots[r], dtype=np.int64)
+        sl = sl[(sl >= 0) & (sl < num_slots)]
+        if sl.size == 0:
+            continue
+        for h in range(hq):
+            g = h // group
+            s = softmax_scale * (kd[sl, g, :] @ q[r, h, :])
+            p = np.exp(s - s.max())
+            out[r, h, :] = output_scale * (p @ vd[sl, g, :]) / p.sum()
+    return out

@@ -389,3 +389,77 @@ def test_pins_catch_planted_mistakes():
 def dataclass_replace(p, **kw):
     import dataclasses
     return dataclasses.replace(p, **kw)
+
+
+# ---------------------------------------------------------------- sparse attention oracle
+# Pins of oracle.sparse_attention by closed forms: a single key gives its value vector,
+# equal scores give the plain mean (numpy.mean, with repeated slots counted twice), a
+# hand-worked two-key case with weights 1/4 and 3/4, slot padding and out-of-range slots
+# take no part, a very large softmax scale gives the arg-max key's value, and grouped
+# query heads read their own KV head.
+
+def _attn_inputs(rows=2, hq=4, hkv=2, num_slots=10, seed=0):
+    rng = np.random.default_rng(seed)
+    q = wl.encode_bf16(rng.standard_normal((rows, hq, 128)))
+    k = wl.encode_e4m3(rng.standard_normal((num_slots, hkv, 128)))
+    v = wl.encode_e4m3(rng.standard_normal((num_slots, hkv, 128)))
+    return q, k, v
+
+
+def test_attn_single_key_is_its_value():
+    q, k, v = _attn_inputs()
+    slots = np.array([[3, -1, -1], [-1, 7, -1]], dtype=np.int32)
+    out = oracle.sparse_attention(q, k, v, slots, 0.3, 2.0)
+    vd = oracle.decode_e4m3(v)
+    for h in range(4):
+        assert np.array_equal(out[0, h], 2.0 * vd[3, h // 2])
+        assert np.array_equal(out[1, h], 2.0 * vd[7, h // 2])
+
+
+def test_attn_equal_scores_is_the_mean_with_repeats():
+    _, k, v = _attn_inputs(rows=1)
+    q = np.zeros((1, 4, 128), dtype=np.uint16)                 # every score 0
+    slots = np.array([[2, 5, 5, 9, -1, 11, 0]], dtype=np.int32)  # 11 is out of range
+    out = oracle.sparse_attention(q, k, v, slots, 1.0, 1.0)
+    vd = oracle.decode_e4m3(v)
+    for h in range(4):
+        ref = np.mean(vd[[2, 5, 5, 9, 0], h // 2, :], axis=0)
+        assert np.allclose(out[0, h], ref, rtol=0, atol=1e-12)
+
+
+def test_attn_two_keys_hand_worked():
+    """q = e0, k0 = 0, k1 = e0, softmax scale ln 3: scores 0 and ln 3, weights 1/4 and 3/4;
+    v0 = 1, v1 = 2 at d = 0 gives 1.75, and v0 = -4, v1 = 4 at d = 5 gives 2."""
+    q = np.zeros((1, 1, 128)); q[0, 0, 0] = 1.0
+    k = np.zeros((2, 1, 128)); k[1, 0, 0] = 1.0
+    v = np.zeros((2, 1, 128)); v[0, 0, 0], v[1, 0, 0] = 1.0, 2.0; v[0, 0, 5], v[1, 0, 5] = -4.0, 4.0
+    out = oracle.sparse_attention(wl.encode_bf16(q), wl.encode_e4m3(k), wl.encode_e4m3(v),
+                                  np.array([[0, 1]], dtype=np.int32), math.log(3.0), 1.0)
+    assert abs(out[0, 0, 0] - 1.75) < 1e-12
+    assert abs(out[0, 0, 5] - 2.0) < 1e-12
+    assert np.all(out[0, 0, [1, 2, 3, 4, 6]] == 0.0)
+
+
+def test_attn_padding_and_argmax_limit():
+    q, k, v = _attn_inputs(rows=2, seed=3)
+    slots = np.array([[-1, -1, 40, -7], [1, 4, 6, 8]], dtype=np.int32)
+    out = oracle.sparse_attention(q, k, v, slots, 1e4, 1.0)
+    assert np.all(out[0] == 0.0)                                  # nothing valid: zeros
+    qd, kd, vd = oracle.decode_bf16(q), oracle.decode_e4m3(k), oracle.decode_e4m3(v)
+    for h in range(4):
+        g = h // 2
+        dots = kd[[1, 4, 6, 8], g, :] @ qd[1, h, :]
+        top = [1, 4, 6, 8][int(np.argmax(dots))]
+        if np.sort(dots)[-1] - np.sort(dots)[-2] > 1e-2:           # a clear winner
+            assert np.allclose(out[1, h], vd[top, g], rtol=0, atol=1e-9)
+
+
+def test_attn_grouped_heads_read_their_kv_head():
+    _, k, v = _attn_inputs(rows=1, hq=6, hkv=3, seed=5)
+    q = np.zeros((1, 6, 128), dtype=np.uint16)
+    slots = np.array([[4]], dtype=np.int32)
+    out = oracle.sparse_attention(q, k, v, slots, 1.0, 1.0)
+    vd = oracle.decode_e4m3(v)
+    for h in range(6):
+        assert np.array_equal(out[0, h], vd[4, h // 2])
+        assert not np.array_equal(out[0, h], vd[4, (h // 2 + 1) % 3])
