@@ -100,7 +100,8 @@ def timed_ms(fn, iters, flush=None):
 def secondary_legs(dev, iters=20):
     """Selection (HBM-bound) and materialised scoring, measured beside the fused path:
     idx_select on the selection workload (64 rows, pitch 131072) and on the prefill
-    workload's materialised scores (4096 x 65536 fp32, 1.04 GB), idx_score on prefill.
+    workload's materialised scores (4096 x 65536 fp32, 1.04 GB), idx_score on prefill, and
+    the consumer, idx_sparse_attn (512 rows x 2048 selected slots; HBM-bound gather).
     Cold numbers flush L2 and the 256 MB MALL with a 512 MiB fill before every call."""
     import torch
     import sparse_attention_indexer_score_amd as sai
@@ -151,7 +152,30 @@ def secondary_legs(dev, iters=20):
         "cold_GBps": round(nbytes / (cold * 1e-3) / 1e9, 1),
         "hbm_frac": round(nbytes / (cold * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     log(f"[bench] select over materialised prefill scores: cold {cold:.4f} ms")
-    del sel, sr, dpp, flush_buf
+    del sel, sr, dpp
+    torch.cuda.empty_cache()
+
+    # The consumer: sparse attention of 512 decode rows over their 2048 selected slots.
+    a = wl.make("sparse_attn")
+    q = torch.from_numpy(a.q.view(np.int16)).to(dev)
+    kc, vc = torch.from_numpy(a.k_cache).to(dev), torch.from_numpy(a.v_cache).to(dev)
+    sl = torch.from_numpy(a.slots).to(dev)
+    out = torch.empty((a.rows, a.q.shape[1], 128), dtype=torch.float32, device=dev)
+    att = lambda: sai.idx_sparse_attn(q, kc, vc, sl, a.softmax_scale, a.output_scale, out=out)
+    att()
+    torch.cuda.synchronize()
+    hkv = a.k_cache.shape[1]
+    valid = int(((a.slots >= 0) & (a.slots < a.k_cache.shape[0])).sum())
+    nbytes = valid * hkv * 2 * 128 + a.slots.size * 4 + a.q.size * 2 + out.numel() * 4
+    cold, cold_min = timed_ms(att, iters, flush)
+    res["sparse_attn"] = {
+        "what": f"idx_sparse_attn, {a.rows} rows x {a.slots.shape[1]} selected slots, {a.q.shape[1]} query / {hkv} KV "
+                f"heads, head_dim 128, e4m3 KV cache of {a.k_cache.shape[0]} slots",
+        "bytes": nbytes, "cold_ms": round(cold, 4), "cold_min_ms": round(cold_min, 4),
+        "cold_GBps": round(nbytes / (cold * 1e-3) / 1e9, 1),
+        "hbm_frac": round(nbytes / (cold * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    log(f"[bench] sparse attention: cold {cold:.4f} ms")
+    del q, kc, vc, sl, out, flush_buf
     torch.cuda.empty_cache()
     return res
 

@@ -207,6 +207,29 @@ size_t idx_fused_workspace(const idx_problem* p, int32_t k);
 int idx_page_slots(const int32_t* idx, int32_t rows, int32_t k, const int32_t* ks, const int32_t* page_table,
                    const int32_t* row_req, int32_t max_pages, int32_t* out, void* stream);
 
+/* ------------------------------------------------------------------ consumer
+ * idx_sparse_attn — attention of each query row over only the KV slots its indexer
+ * selected (QSA sparse paged attention page, vllm-project/vllm#66512: about 2048 tokens
+ * per row chosen by the indexer; slots are physical, as idx_page_slots returns them;
+ * QK in bf16 and PV in fp16 with the e4m3 cache values converted exactly, fp32
+ * accumulation):
+ *     s_j      = softmax_scale * q[r, h] . k_cache[slot_j, g],   g = h / (hq / hkv)
+ *     out[r,h] = output_scale * sum_j exp(s_j - max) v_cache[slot_j, g] / sum_j exp(s_j - max)
+ * over the valid slots of row r.
+ *   q        bf16 bit patterns [rows][hq][128]
+ *   k_cache, v_cache  e4m3 (OCP E4M3FN) [num_slots][hkv][128]
+ *   slots    int32 [rows][width]; an entry outside [0, num_slots) (such as the -1 of a
+ *            short selection) takes no part; a row with no valid entry gives zeros
+ *   out      fp32 [rows][hq][128]
+ * The softmax weights enter the PV product rounded to fp16 (relative error <= 2^-11 per
+ * weight).  One workgroup per (row, KV head); no workspace.  Errors: IDX_EINVAL (rows < 0,
+ * width < 0, hkv < 1, hq not a multiple of hkv, hq / hkv > 32, num_slots < 1, rows * hkv
+ * >= 2^31, a non-finite scale, a null pointer with rows > 0), IDX_EALIGN (q, k_cache,
+ * v_cache not 16-byte aligned; out or slots not 4-byte aligned).                     */
+int idx_sparse_attn(const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_cache, int64_t num_slots,
+                    const int32_t* slots, int32_t rows, int32_t hq, int32_t hkv, int32_t width, float softmax_scale,
+                    float output_scale, float* out, void* stream);
+
 /* ------------------------------------------------------------------ measurement
  * Stage timing of idx_fused_topk for benchmarks.  While enabled, every idx_fused_topk
  * call (any thread) records six HIP events on its own stream at its stage boundaries,

@@ -80,6 +80,8 @@ def _lib():
             "idx_fused_topk": (ctypes.c_int, [P, i32, _c_p, _c_p, sz, ctypes.POINTER(IdxStats), _c_p]),
             "idx_fused_workspace": (sz, [P, i32]),
             "idx_page_slots": (ctypes.c_int, [_c_p, i32, i32, _c_p, _c_p, _c_p, i32, _c_p, _c_p]),
+            "idx_sparse_attn": (ctypes.c_int, [_c_p, _c_p, _c_p, i64, _c_p, i32, i32, i32, i32, ctypes.c_float,
+                                               ctypes.c_float, _c_p, _c_p]),
             "idx_strerror": (ctypes.c_char_p, [ctypes.c_int]),
             "idx_version": (i32, []),
             "idx_timing_enable": (ctypes.c_int, [i32]),
@@ -325,6 +327,27 @@ def idx_page_slots(idx: torch.Tensor, page_table: torch.Tensor, row_req: torch.T
         out = torch.empty_like(idx)
     _check(_lib().idx_page_slots(_ptr(idx), rows, k, _ptr(ks), _ptr(page_table), _ptr(row_req),
                                  page_table.shape[1], _ptr(out), _stream(stream)), "idx_page_slots")
+    return out
+
+
+def idx_sparse_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, slots: torch.Tensor,
+                    softmax_scale: float, output_scale: float = 1.0, out: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """Attention of each query row over its selected KV slots (the top-k's consumer).
+    q: bf16 bit patterns [rows, hq, 128] (int16/uint16 or bfloat16); k_cache, v_cache: e4m3 bytes
+    [num_slots, hkv, 128] (uint8); slots: int32 [rows, width], entries outside [0, num_slots)
+    ignored.  Returns fp32 [rows, hq, 128]."""
+    assert q.dim() == 3 and q.shape[2] == 128 and q.element_size() == 2 and q.is_contiguous()
+    assert k_cache.dtype == torch.uint8 and k_cache.dim() == 3 and k_cache.is_contiguous()
+    assert v_cache.shape == k_cache.shape and v_cache.dtype == torch.uint8 and v_cache.is_contiguous()
+    assert slots.dtype == torch.int32 and slots.dim() == 2 and slots.is_contiguous()
+    rows, hq, _ = q.shape
+    num_slots, hkv, _ = k_cache.shape
+    if out is None:
+        out = torch.empty((rows, hq, 128), dtype=torch.float32, device=q.device)
+    _check(_lib().idx_sparse_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), num_slots, _ptr(slots), rows, hq, hkv,
+                                  slots.shape[1], float(softmax_scale), float(output_scale), _ptr(out),
+                                  _stream(stream)), "idx_sparse_attn")
     return out
 
 

@@ -1,5 +1,6 @@
 // C ABI of libidx.so: argument validation, workspace sizing and carve-up, dispatch of the
 // gfx950 kernels.  No device memory is allocated here; the caller owns every buffer.
+#include <cmath>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -236,6 +237,24 @@ int idx_page_slots(const int32_t* idx, int32_t rows, int32_t k, const int32_t* k
   if (rc) return rc;
   return hip_err(launch_page_slots(idx, rows, k, ks, page_table, row_req, max_pages, out,
                                    static_cast<hipStream_t>(stream)));
+}
+
+int idx_sparse_attn(const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_cache, int64_t num_slots,
+                    const int32_t* slots, int32_t rows, int32_t hq, int32_t hkv, int32_t width, float softmax_scale,
+                    float output_scale, float* out, void* stream) {
+  if (rows < 0 || width < 0 || hkv < 1 || hq < 1 || hq % hkv != 0 || hq / hkv > 32 || num_slots < 1)
+    return IDX_EINVAL;
+  if ((int64_t)rows * hkv > 0x7FFFFFFF) return IDX_EINVAL;
+  if (!std::isfinite(softmax_scale) || !std::isfinite(output_scale)) return IDX_EINVAL;
+  if (rows == 0) return IDX_OK;
+  if (!q || !k_cache || !v_cache || !out || (width > 0 && !slots)) return IDX_EINVAL;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 4) ||
+      (slots && !aligned(slots, 4)))
+    return IDX_EALIGN;
+  int rc = current_device(nullptr);
+  if (rc) return rc;
+  return hip_err(launch_sparse_attn(q, k_cache, v_cache, num_slots, slots, rows, hq, hkv, width, softmax_scale,
+                                    output_scale, out, static_cast<hipStream_t>(stream)));
 }
 
 size_t idx_score_workspace(const idx_problem* p) {

@@ -62,6 +62,9 @@ hipError_t launch_select_single(const float* x, int64_t ld, const int32_t* row_s
 hipError_t launch_select_split(const float* x, int64_t ld, const int32_t* row_start, const int32_t* len,
                                int32_t rows, int32_t k, int32_t g, int32_t* out, void* ws, hipStream_t s);
 size_t select_split_ws_bytes(int32_t rows);
+hipError_t launch_sparse_attn(const uint16_t* q, const uint8_t* k, const uint8_t* v, int64_t num_slots,
+                              const int32_t* slots, int32_t rows, int32_t hq, int32_t hkv, int32_t width,
+                              float softmax_scale, float output_scale, float* out, hipStream_t s);
 
 // Score-kernel work decomposition shared with the host sizing code.
 int rows_per_block(int heads, int fmt);

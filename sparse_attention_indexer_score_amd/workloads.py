@@ -294,12 +294,51 @@ def select_only(rows=64, ld=131072, min_len=2048, topk=2048, seed=2, runs=64, ru
     return SelectProblem("select", np.ascontiguousarray(x), length, topk)
 
 
+@dataclasses.dataclass
+class AttnProblem:
+    """Inputs of the sparse attention consumer: q bf16 bits [rows, hq, 128], e4m3 K and V
+    caches [num_slots, hkv, 128], selected physical slots int32 [rows, width] (-1 padded)."""
+    name: str
+    q: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    slots: np.ndarray
+    softmax_scale: float
+    output_scale: float
+
+    @property
+    def rows(self):
+        return self.q.shape[0]
+
+
+def sparse_attn(rows=512, hq=24, hkv=2, width=2048, num_slots=262144, seed=6, short_every=16) -> AttnProblem:
+    """Decode/verify rows attending to `width` selected slots each (the QSA page's shape:
+    2048 selected tokens per row, 24 query heads over 2 KV heads, an fp8 e4m3 KV cache).
+    q ~ N(0, 1) as bf16; K, V ~ N(0, 1) as e4m3; each row's slots are distinct, uniform over
+    the cache.  Every `short_every`-th row keeps a random shorter selection (the rest -1) and
+    the last row has none (a padding row).  softmax_scale = 1/sqrt(128), output_scale = 1."""
+    rq, rk, rv, rs, rn = _streams(seed, 5)
+    q = encode_bf16(rq.standard_normal((rows, hq, HEAD_DIM), dtype=np.float32))
+    k = _normal_e4m3(rk, (num_slots, hkv, HEAD_DIM))
+    v = _normal_e4m3(rv, (num_slots, hkv, HEAD_DIM))
+    slots = np.empty((rows, width), dtype=np.int32)
+    for r in range(rows):
+        slots[r] = rs.choice(num_slots, size=width, replace=False)
+        if short_every and r % short_every == short_every - 1:
+            n = int(rn.integers(0, width + 1))
+            slots[r, n:] = -1
+    if rows:
+        slots[rows - 1] = -1
+    return AttnProblem("sparse_attn", q, k, v, slots, 1.0 / math.sqrt(HEAD_DIM), 1.0)
+
+
 FAMILIES = {
     "tiny": tiny,
     "select": select_only,
     "prefill": prefill,
     "long": long_context,
     "decode": decode,
+    "sparse_attn": sparse_attn,
 }
 
 
