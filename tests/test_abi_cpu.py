@@ -24,7 +24,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("idx_score", "idx_score_workspace", "idx_select", "idx_fused_topk", "idx_select_workspace",
-              "idx_fused_workspace", "idx_page_slots",
+              "idx_fused_workspace", "idx_page_slots", "idx_sparse_attn",
               "idx_strerror", "idx_row_split", "idx_select_split", "idx_version"):
         assert n in names
 
@@ -178,3 +178,25 @@ def test_page_slots_argument_checks():
     assert lib.idx_page_slots(None, 2, 4, None, a, a, 2, a, None) == sai.IDX_EINVAL
     assert lib.idx_page_slots(ctypes.c_void_p(0x10002), 2, 4, None, a, a, 2, a, None) == sai.IDX_EALIGN
     assert lib.idx_page_slots(None, 0, 4, None, None, None, 2, None, None) == 0    # nothing to do
+
+
+def test_sparse_attn_argument_checks():
+    """Host-side validation of idx_sparse_attn; every case returns before any device call."""
+    lib = sai.library()
+    a = ctypes.c_void_p(0x10000)
+    f = lambda q=a, kc=a, vc=a, ns=100, sl=a, rows=2, hq=24, hkv=2, width=8, ss=0.1, os_=1.0, out=a: \
+        lib.idx_sparse_attn(q, kc, vc, ns, sl, rows, hq, hkv, width, ss, os_, out, None)
+    assert f(rows=-1) == sai.IDX_EINVAL
+    assert f(width=-1) == sai.IDX_EINVAL
+    assert f(hkv=0) == sai.IDX_EINVAL
+    assert f(hq=25) == sai.IDX_EINVAL                    # not a multiple of hkv
+    assert f(hq=66, hkv=2) == sai.IDX_EINVAL             # 33 query heads per KV head
+    assert f(ns=0) == sai.IDX_EINVAL
+    assert f(ss=float("nan")) == sai.IDX_EINVAL
+    assert f(os_=float("inf")) == sai.IDX_EINVAL
+    assert f(q=None) == sai.IDX_EINVAL
+    assert f(sl=None) == sai.IDX_EINVAL                  # slots needed when width > 0
+    assert f(q=ctypes.c_void_p(0x10008)) == sai.IDX_EALIGN
+    assert f(kc=ctypes.c_void_p(0x10004)) == sai.IDX_EALIGN
+    assert f(out=ctypes.c_void_p(0x10002)) == sai.IDX_EALIGN
+    assert f(rows=0, q=None, kc=None, vc=None, sl=None, out=None) == 0   # nothing to do
