@@ -163,17 +163,23 @@ __device__ void emit_at_least(const Src& src, int n, int shift, uint64_t prefix,
 }
 
 // Refine the LDS tie list (sm.ntie entries, all sharing the digits above level L) until
-// `need` more elements are emitted to out[] through sm.nout.  Contains barriers.
+// `need` more elements are emitted to out[] through sm.nout.  With nz1, the first level
+// normalises the keys it reads (the kept ones are stored normalised for the next levels);
+// with zeroed, the caller has already cleared the first level's histogram.  Contains
+// barriers.
 template <int NT, class SM>
-__device__ void refine_lds(int L, uint32_t need, int32_t* out, SM& sm) {
+__device__ void refine_lds(int L, uint32_t need, int32_t* out, SM& sm, const KeyNorm* nz1 = nullptr,
+                           bool zeroed = false) {
   constexpr int PER = (SM::kCap + NT - 1) / NT;
-  for (;; ++L) {
+  for (bool first = true;; ++L, first = false) {
     const Level lv = level_of(L);
     const int nbins = 1 << lv.width;
     const uint32_t dmask = (uint32_t)nbins - 1;
     const int nt = sm.ntie;
-    zero_hist<NT>(sm, nbins);
-    __syncthreads();
+    if (!(first && zeroed)) {
+      zero_hist<NT>(sm, nbins);
+      __syncthreads();
+    }
     uint32_t k_[PER];
     int32_t i_[PER];
 #pragma unroll
@@ -181,6 +187,7 @@ __device__ void refine_lds(int L, uint32_t need, int32_t* out, SM& sm) {
       const int t = (int)threadIdx.x + e * NT;
       if (t < nt) {
         k_[e] = sm.tkey[t];
+        if (first && nz1) k_[e] = nz1->normalize(k_[e]);
         i_[e] = sm.tidx[t];
         atomicAdd(&sm.hist[(uint32_t)(composite_key(k_[e], i_[e]) >> lv.shift) & dmask], 1u);
       }
@@ -472,6 +479,7 @@ __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out,
     sm.nout = 0;
     sm.kmax = 0u;
   }
+  zero_hist<NT>(sm, kHistBins);  // for the refinement (the streaming pass does not use it)
   __syncthreads();
   uint32_t kmax = 0u;
   // Appends the lanes' keys k_[u] (element ix_[u]) that pass, one LDS atomic per wave.
@@ -547,9 +555,7 @@ __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out,
   const KeyNorm nz = key_norm(T, sm.kmax);
   __syncthreads();
   if (c >= m && c <= SM::kCap) {
-    for (int t = threadIdx.x; t < c; t += NT) sm.tkey[t] = nz.normalize(sm.tkey[t]);
-    __syncthreads();
-    refine_lds<NT>(1, (uint32_t)m, out, sm);
+    refine_lds<NT>(1, (uint32_t)m, out, sm, &nz, true);  // keys normalised over [T, max] as read
   } else {
     block_select<NT>(RowSrc{x}, n, m, out, sm);
   }
