@@ -85,6 +85,12 @@ struct KeyNorm {
 __device__ __forceinline__ KeyNorm key_norm(uint32_t lo, uint32_t hi) {
   return KeyNorm{lo, hi == lo ? 32 : __builtin_clz(hi - lo)};
 }
+struct NormLdsKeySrc {  // raw order keys in LDS, normalised as they are read; index = position
+  const uint32_t* k;
+  KeyNorm nz;
+  __device__ __forceinline__ uint32_t key(int j) const { return nz.normalize(k[j]); }
+  __device__ __forceinline__ int32_t index(int j) const { return j; }
+};
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
@@ -375,7 +381,7 @@ __device__ void block_select(const Src& src, int n, int m, int32_t* out, SM& sm)
 // over the input.  Returns the key in every thread; with fewer levels, the smallest key of
 // the m-th key's bin at the last level (a lower bound of the m-th key).  Contains barriers.
 template <int NT, class Src, class SM, int LEVELS = 3>
-__device__ uint32_t block_kth_key(const Src& src, int n, int m, SM& sm) {
+__device__ uint32_t block_kth_key(const Src& src, int n, int m, SM& sm, bool zeroed = false) {
   uint32_t prefix = 0;
   int above_shift = 32;
   uint32_t need = (uint32_t)m;
@@ -385,8 +391,10 @@ __device__ uint32_t block_kth_key(const Src& src, int n, int m, SM& sm) {
   for (int L = 0; L < LEVELS; ++L) {
     const int sh = shifts[L];
     const int nbins = 1 << widths[L];
-    zero_hist<NT>(sm, nbins);
-    __syncthreads();
+    if (!(L == 0 && zeroed)) {  // (zeroed: the caller cleared the first level's histogram)
+      zero_hist<NT>(sm, nbins);
+      __syncthreads();
+    }
     for (int base = 0; base < n; base += NT) {
       const int j = base + (int)threadIdx.x;
       if (j < n) {
@@ -465,13 +473,13 @@ __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out,
       atomicMin(&sm.kmin, lo);
       atomicMax(&sm.kmax, hi);
     }
+    zero_hist<NT>(sm, kHistBins);  // the sample's radix level, cleared under the same barrier
     __syncthreads();
     const KeyNorm nz = key_norm(sm.kmin, sm.kmax);
-    for (int t = threadIdx.x; t < kSelSamples; t += NT) sm.tkey[t] = nz.normalize(sm.tkey[t]);
-    __syncthreads();
     int64_t rank = ((int64_t)7 * m * kSelSamples + (int64_t)4 * n - 1) / ((int64_t)4 * n);  // ceil(1.75 m S / n)
     rank = rank < 1 ? 1 : (rank > kSelSamples ? kSelSamples : rank);
-    T = nz.denormalize(block_kth_key<NT, LdsKeySrc, SM, 1>(LdsKeySrc{sm.tkey}, kSelSamples, (int)rank, sm));
+    T = nz.denormalize(block_kth_key<NT, NormLdsKeySrc, SM, 1>(NormLdsKeySrc{sm.tkey, nz}, kSelSamples, (int)rank,
+                                                                 sm, true));
     __syncthreads();
   }
   if (threadIdx.x == 0) {
