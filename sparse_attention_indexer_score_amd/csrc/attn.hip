@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(AttnArgs P
   };
 
   uint8_t* vt = sh.vt[wave];
-  Tile cur, nxt;
+  Tile cur, nxt = {};  // (nxt defined even when no tile is left to fetch into it)
   int t = wave;
   if (t < ntiles) fetch(t, cur);
   for (; t < ntiles; t += kAttnWaves) {
