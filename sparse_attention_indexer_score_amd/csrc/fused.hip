@@ -1002,12 +1002,34 @@ __global__ __launch_bounds__(kThrThreads) void threshold_kernel(ThrArgs T) {
       // LDS for the two histogram passes.
       const bool staged = n <= kThrStage;  // workgroup-uniform (never for kThrStage == 0)
       uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+      if constexpr (kThrStage > 0) {
+        if (staged) {
+          // Every load of the pass issued before any is used: one memory round trip.
+          constexpr int PER = (kThrStage + kThrThreads - 1) / kThrThreads;
+          uint32_t kv[PER];
+#pragma unroll
+          for (int e = 0; e < PER; ++e) {
+            const int j = (int)threadIdx.x + e * kThrThreads;
+            kv[e] = order_key(sp[j < n ? j : n - 1]);  // unconditional (n >= 1): no branch per load
+          }
+#pragma unroll
+          for (int e = 0; e < PER; ++e) {
+            const int j = (int)threadIdx.x + e * kThrThreads;
+            if (j < n) {
+              skey[j] = kv[e];
+              lo = min(lo, kv[e]);
+              hi = max(hi, kv[e]);
+            }
+          }
+        }
+      }
+      if (!staged) {
 #pragma unroll 4
-      for (int j = threadIdx.x; j < n; j += kThrThreads) {
-        const uint32_t k = order_key(sp[j]);
-        if (staged) skey[j] = k;
-        lo = min(lo, k);
-        hi = max(hi, k);
+        for (int j = threadIdx.x; j < n; j += kThrThreads) {
+          const uint32_t k = order_key(sp[j]);
+          lo = min(lo, k);
+          hi = max(hi, k);
+        }
       }
       auto key_at = [&](int j) -> uint32_t { return staged ? skey[j] : order_key(sp[j]); };
       lo = wave_min_u32(lo);
