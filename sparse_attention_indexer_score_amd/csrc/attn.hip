@@ -27,7 +27,8 @@ namespace idx {
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 constexpr int kAttnWaves = 4;
 constexpr int kAttnThreads = kAttnWaves * kWave;
@@ -56,18 +57,22 @@ struct AttnShared {
   };
 };
 
-// 8 e4m3 bytes (two words, byte e = element e) as bf16 / fp16 operands; both conversions are
-// exact (every e4m3 value is a bf16 and an fp16 value).
-template <bool HI>
-__device__ __forceinline__ v2f fp8x2(uint32_t w) { return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI); }
+// 8 e4m3 bytes (two words, byte e = element e) as bf16 / fp16 operands, two values per
+// conversion instruction (scale 1.0); both conversions are exact (every e4m3 value is a
+// bf16 and an fp16 value).
 __device__ __forceinline__ v8bf e4m3x8_bf16(uint32_t w0, uint32_t w1) {
-  const v2f a = fp8x2<false>(w0), b = fp8x2<true>(w0), c = fp8x2<false>(w1), d = fp8x2<true>(w1);
-  return v8bf{(__bf16)a.x, (__bf16)a.y, (__bf16)b.x, (__bf16)b.y, (__bf16)c.x, (__bf16)c.y, (__bf16)d.x, (__bf16)d.y};
+  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, false);
+  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, true);
+  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, false);
+  const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, true);
+  return v8bf{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 __device__ __forceinline__ v8h e4m3x8_f16(uint32_t w0, uint32_t w1) {
-  const v2f a = fp8x2<false>(w0), b = fp8x2<true>(w0), c = fp8x2<false>(w1), d = fp8x2<true>(w1);
-  return v8h{(_Float16)a.x, (_Float16)a.y, (_Float16)b.x, (_Float16)b.y,
-             (_Float16)c.x, (_Float16)c.y, (_Float16)d.x, (_Float16)d.y};
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w0, 1.0f, false);
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w0, 1.0f, true);
+  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w1, 1.0f, false);
+  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w1, 1.0f, true);
+  return v8h{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
 // Position of key c (0..31) of a tile in the MFMA K order of the PV product: key
@@ -170,11 +175,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(AttnArgs P
     l_run = alpha * l_run + psum;
     m_run = m_new;
     // Rescale the outputs: O row (head) 8 (i / 4) + 4 h + (i % 4) takes that head's factor.
+    // Skipped when no head's maximum moved (every factor 1), as in most tiles after the first.
+    if (wave_ballot(alpha != 1.0f)) {  // wave-uniform
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float ai = __shfl(alpha, 8 * (i >> 2) + 4 * h + (i & 3), kWave);
+      for (int i = 0; i < 16; ++i) {
+        const float ai = __shfl(alpha, 8 * (i >> 2) + 4 * h + (i & 3), kWave);
 #pragma unroll
-      for (int n = 0; n < 4; ++n) o[n][i] *= ai;
+        for (int n = 0; n < 4; ++n) o[n][i] *= ai;
+      }
     }
     // PV: two K-steps of 16 keys, four N-tiles of 32 dims.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
