@@ -443,11 +443,15 @@ __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out,
   const float4* xv = reinterpret_cast<const float4*>(x);
   const int nv = vec ? n / 4 : 0;
   float4 cur[UV], nxt[UV];
+  // Unconditional loads (lanes past the end re-read the last vector and are masked when
+  // tested): a load under a branch would leave the compiler unable to count the loads in
+  // flight, and it would then wait for the step issued ahead before testing this one.
+  // Needs nv >= 1.
   auto load = [&](float4* v, int base) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < UV; ++u) {
       const int jv = base + u * NT + (int)threadIdx.x;
-      v[u] = jv < nv ? xv[jv] : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[u] = xv[jv < nv ? jv : nv - 1];
     }
   };
   if (nv > 0) load(cur, 0);
@@ -520,7 +524,7 @@ __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out,
   };
   // Vector part: one append (one LDS atomic per wave) for all 4 * UV keys of a step.
   for (int base = 0; base < nv; base += UV * NT) {
-    if (base + UV * NT < nv) load(nxt, base + UV * NT);
+    load(nxt, base + UV * NT);  // past the end on the last step: re-reads of the last vector
     uint32_t k_[4 * UV];
     bool ok[4 * UV];
     int ix_[4 * UV];
