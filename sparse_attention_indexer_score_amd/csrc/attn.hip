@@ -112,27 +112,38 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(AttnArgs P
     uint4 kr[4], vr[4];
     bool valid;
   };
-  // Slot of key c of tile t and its K / V bytes [64 h, 64 h + 64) (zeros when not valid).
-  auto fetch = [&](int t, Tile& T) {
+  // Every load below is unconditional (a position past the row's end re-reads its last slot
+  // id, an invalid slot reads slot 0, and the tile's valid flag masks what was read): a load
+  // under a branch would leave the compiler unable to count the loads in flight, and each
+  // tile would then wait for the prefetch of the next before its first MFMA.
+  auto slot_at = [&](int t) -> int32_t {
     const int j = t * kAttnTile + c;
-    const int64_t slot = j < P.width ? (int64_t)srow[j] : -1;
-    T.valid = slot >= 0 && slot < P.num_slots;
-    const int64_t base = ((T.valid ? slot : 0) * P.hkv + g) * kHeadDim + 64 * h;
+    return srow[j < P.width ? j : P.width - 1];
+  };
+  // K / V bytes [64 h, 64 h + 64) of key c of tile t, whose slot id was loaded before.
+  auto fetch = [&](int t, int32_t slot, Tile& T) {
+    T.valid = t * kAttnTile + c < P.width && slot >= 0 && slot < P.num_slots;
+    const int64_t base = ((int64_t)(T.valid ? slot : 0) * P.hkv + g) * kHeadDim + 64 * h;
     const uint4* kp = reinterpret_cast<const uint4*>(P.k + base);
     const uint4* vp = reinterpret_cast<const uint4*>(P.v + base);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      T.kr[u] = T.valid ? kp[u] : make_uint4(0, 0, 0, 0);
-      T.vr[u] = T.valid ? vp[u] : make_uint4(0, 0, 0, 0);
+      T.kr[u] = kp[u];
+      T.vr[u] = vp[u];
     }
   };
 
   uint8_t* vt = sh.vt[wave];
-  Tile cur, nxt = {};  // (nxt defined even when no tile is left to fetch into it)
+  Tile cur, nxt;
   int t = wave;
-  if (t < ntiles) fetch(t, cur);
+  int32_t sn = 0;  // slot id of this lane's key in the tile after the next
+  if (ntiles > 0) {  // (P.width >= 1: the clamped slot reads stay in the row)
+    fetch(t, slot_at(t), cur);
+    sn = slot_at(t + kAttnWaves);
+  }
   for (; t < ntiles; t += kAttnWaves) {
-    if (t + kAttnWaves < ntiles) fetch(t + kAttnWaves, nxt);
+    fetch(t + kAttnWaves, sn, nxt);  // past the last tile: masked re-reads
+    sn = slot_at(t + 2 * kAttnWaves);
     // QK over the tile.
     v16f sacc = {};
 #pragma unroll
@@ -146,7 +157,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(AttnArgs P
       const int pos = vt_pos(c);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint32_t wd[4] = {cur.vr[u].x, cur.vr[u].y, cur.vr[u].z, cur.vr[u].w};
+        const uint4 v = cur.valid ? cur.vr[u] : make_uint4(0, 0, 0, 0);  // (an invalid key's V may be any bytes)
+        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int b = 0; b < 16; ++b) vt[(64 * h + 16 * u + b) * kVtStride + pos] = (uint8_t)(wd[b >> 2] >> (8 * (b & 3)));
       }
