@@ -1121,10 +1121,22 @@ __global__ __launch_bounds__(kSlabThreads) void slab_select_kernel(SlabArgs S) {
   if (need > 0) {
     __syncthreads();
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-    for (int j = threadIdx.x; j < c; j += kSlabThreads) {
-      const uint32_t k = order_key(ss[j]);
-      lo = min(lo, k);
-      hi = max(hi, k);
+    // 8 loads per thread in flight per step, unconditional: a lane past the end re-reads the
+    // last candidate (c >= need >= 1), which leaves the minimum and maximum unchanged.
+    constexpr int U = 8;
+    for (int base = 0; base < c; base += U * kSlabThreads) {
+      float v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = base + u * kSlabThreads + (int)threadIdx.x;
+        v[u] = ss[j < c ? j : c - 1];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t k = order_key(v[u]);
+        lo = min(lo, k);
+        hi = max(hi, k);
+      }
     }
     lo = wave_min_u32(lo);
     hi = wave_max_u32(hi);

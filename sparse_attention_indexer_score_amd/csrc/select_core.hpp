@@ -313,9 +313,16 @@ __device__ __forceinline__ void hist_level1(const Src& src, int n, SM& sm) {
 #pragma unroll
     for (int u = 0; u < U; ++u) atomicAdd(&sm.hist[k_[u] >> (32 - kHistBits)], 1u);
   }
-  for (; base < n; base += NT) {
-    const int j = base + (int)threadIdx.x;
-    if (j < n) atomicAdd(&sm.hist[src.key(j) >> (32 - kHistBits)], 1u);
+  if (base < n) {  // the rest: clamped loads (a load under a branch waits before the next)
+    uint32_t k_[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = base + u * NT + (int)threadIdx.x;
+      k_[u] = src.key(j < n ? j : n - 1);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (base + u * NT + (int)threadIdx.x < n) atomicAdd(&sm.hist[k_[u] >> (32 - kHistBits)], 1u);
   }
 }
 
@@ -349,24 +356,32 @@ __device__ void block_select(const Src& src, int n, int m, int32_t* out, SM& sm)
     return;
   }
   if (cnt <= (uint32_t)SM::kCap) {
-    for (int base = 0; base < n; base += NT) {
-      const int j = base + (int)threadIdx.x;
-      uint32_t k = 0;
-      int32_t ix = 0;
-      uint32_t d = 0;
-      if (j < n) {
-        k = src.key(j);
-        ix = src.index(j);
-        d = k >> (32 - kHistBits);
+    // U elements per thread and step, loaded unconditionally (clamped; the extra lanes are
+    // masked), so that a step's loads are in flight together.
+    constexpr int U = 4;
+    for (int base = 0; base < n; base += U * NT) {
+      uint32_t k_[U];
+      int32_t ix_[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = base + u * NT + (int)threadIdx.x;
+        const int jj = j < n ? j : n - 1;
+        k_[u] = src.key(jj);
+        ix_[u] = src.index(jj);
       }
-      const bool emit = j < n && d > b1;
-      const bool tie = j < n && d == b1;
-      const int so = wave_append_slot(emit, &sm.nout);
-      if (emit) out[so] = ix;
-      const int st = wave_append_slot(tie, &sm.ntie);
-      if (tie) {
-        sm.tkey[st] = k;
-        sm.tidx[st] = ix;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool in = base + u * NT + (int)threadIdx.x < n;
+        const uint32_t d = k_[u] >> (32 - kHistBits);
+        const bool emit = in && d > b1;
+        const bool tie = in && d == b1;
+        const int so = wave_append_slot(emit, &sm.nout);
+        if (emit) out[so] = ix_[u];
+        const int st = wave_append_slot(tie, &sm.ntie);
+        if (tie) {
+          sm.tkey[st] = k_[u];
+          sm.tidx[st] = ix_[u];
+        }
       }
     }
     __syncthreads();
