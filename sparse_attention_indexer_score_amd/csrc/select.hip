@@ -138,27 +138,35 @@ __global__ __launch_bounds__(kSelThreads) void mb_scatter_kernel(const float* x,
   segment(n, g, part, lo, hi);
   const int64_t off = (int64_t)r * ld + (row_start ? row_start[r] : 0);
   const int l = lane_id();
-  for (int base = lo; base < hi; base += kSelThreads) {
-    const int j = base + (int)threadIdx.x;
-    uint32_t key = 0, d = 0;
-    if (j < hi) {
-      key = order_key(x[off + j]);
-      d = key >> (32 - kHistBits);
+  // U elements per thread and step, loaded unconditionally at clamped positions (a load under
+  // a branch is waited for before the next is issued); lanes past the end are masked.
+  constexpr int U = 4;
+  for (int base = lo; base < hi; base += U * kSelThreads) {
+    uint32_t key_[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = base + u * kSelThreads + (int)threadIdx.x;
+      key_[u] = order_key(x[off + (j < hi ? j : hi - 1)]);
     }
-    const uint64_t me = wave_ballot(j < hi && (d > b1 || (all_bin && d == b1)));
-    const uint64_t mt = wave_ballot(j < hi && keep_ties && d == b1);
-    int be = 0, bt = 0;
-    if (l == 0) {
-      if (me) be = atomicAdd(&sm.nout, __builtin_popcountll(me));
-      if (mt) bt = atomicAdd(&sm.ntie, __builtin_popcountll(mt));
-    }
-    be = readlane(be, 0);
-    bt = readlane(bt, 0);
-    if ((me >> l) & 1) eidx[be + mask_prefix(me)] = j;
-    if ((mt >> l) & 1) {
-      const int t = bt + mask_prefix(mt);
-      sm.tkey[t] = key;
-      sm.tidx[t] = j;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = base + u * kSelThreads + (int)threadIdx.x;
+      const uint32_t key = key_[u], d = key >> (32 - kHistBits);
+      const uint64_t me = wave_ballot(j < hi && (d > b1 || (all_bin && d == b1)));
+      const uint64_t mt = wave_ballot(j < hi && keep_ties && d == b1);
+      int be = 0, bt = 0;
+      if (l == 0) {
+        if (me) be = atomicAdd(&sm.nout, __builtin_popcountll(me));
+        if (mt) bt = atomicAdd(&sm.ntie, __builtin_popcountll(mt));
+      }
+      be = readlane(be, 0);
+      bt = readlane(bt, 0);
+      if ((me >> l) & 1) eidx[be + mask_prefix(me)] = j;
+      if ((mt >> l) & 1) {
+        const int t = bt + mask_prefix(mt);
+        sm.tkey[t] = key;
+        sm.tidx[t] = j;
+      }
     }
   }
   __syncthreads();
