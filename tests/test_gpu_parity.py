@@ -224,8 +224,9 @@ def test_select_all_equal_rows_force_rescan():
         assert_same_sets(got, ref, f"split={split}")
 
 
-def _sample_positions(n, seg=64, nseg=64):
-    """Positions the single-workgroup select samples (runs of 64 at evenly spaced starts)."""
+def _sample_positions(n, seg=64, nseg=32):
+    """Positions the single-workgroup select samples: 32 runs of 64 consecutive elements,
+    run g starting at floor(g (n - 64) / 31)."""
     starts = [i * (n - seg) // (nseg - 1) for i in range(nseg)]
     return np.concatenate([np.arange(a, a + seg) for a in starts])
 
@@ -245,7 +246,7 @@ def test_select_sampled_threshold_misjudged(workspace):
     x[1] += 1.0                                                                  # count(>= T) > buffer
     x[1, pos] = rng.uniform(0.0, 0.5, size=len(pos)).astype(np.float32)
     x[2, :] = np.float32(0.25)                                                   # all equal: rescan
-    x[3, pos] = np.float32(0.75)                                                 # 4096 equal sample values
+    x[3, pos] = np.float32(0.75)                                                 # 2048 equal sample values
     n = np.array([ld, ld, ld, ld, 6000], dtype=np.int32)
     ref = oracle.select_rows(x, n, k)
     got = sai.idx_select(torch.from_numpy(x).cuda(), torch.from_numpy(n).cuda(), k, split=0,
@@ -262,6 +263,23 @@ def test_select_short_and_empty_rows(workspace):
     got = sai.idx_select(torch.from_numpy(x).cuda(), torch.from_numpy(n).cuda(), 64,
                          workspace=workspace).cpu().numpy()
     assert_same_sets(got, ref)
+
+
+@pytest.mark.parametrize("split", [0, 4])
+def test_select_sampled_rows_ragged_and_unaligned(split):
+    """Sampled rows (longer than the 6144-entry candidate buffer) whose streaming pass ends in
+    a partial step, with starts 0-3 floats past a 16-byte boundary (unaligned rows take the
+    4-byte path): the loads past the end are clamped re-reads that must not be selected."""
+    rng = np.random.default_rng(31)
+    ld = 70000
+    x = rng.standard_normal((8, ld)).astype(np.float32)
+    rs = np.array([0, 1, 2, 3, 4, 0, 5, 0], dtype=np.int32)
+    n = np.array([6145, 6145, 16383, 16385, 65537, 4097 * 4 + 3, 60000, 1], dtype=np.int32)
+    k = 2048
+    ref = oracle.select_rows(x, n, k, row_start=rs)
+    got = sai.idx_select(torch.from_numpy(x).cuda(), torch.from_numpy(n).cuda(), k,
+                         row_start=torch.from_numpy(rs).cuda(), split=split).cpu().numpy()
+    assert_same_sets(got, ref, f"split={split}")
 
 
 def test_select_row_start_offsets():
