@@ -56,6 +56,27 @@ def test_attn_small_ragged():
     check(a)
 
 
+def test_attn_masked_reads_do_not_leak():
+    """Invalid slots (negative, past the cache) and the positions past the row's width in its
+    last tile are read from slot 0 and masked. No row selects slot 0, so the output must not
+    change, bit for bit, when slot 0's K and V bytes are e4m3 NaN codes instead of zeros."""
+    a = wl.sparse_attn(rows=16, width=200, num_slots=3000, seed=12, short_every=3)
+    a.slots[a.slots == 0] = 1
+    a.slots[2, ::5] = -7
+    a.slots[3, ::3] = 3000 + 5
+    a.k_cache[0] = 0
+    a.v_cache[0] = 0
+    clean = run_gpu(a)
+    a.k_cache[0] = 0x7F
+    a.v_cache[0] = 0x7F
+    poisoned = run_gpu(a)
+    assert np.isfinite(poisoned).all()
+    assert np.array_equal(poisoned, clean)
+    a.k_cache[0] = 0
+    a.v_cache[0] = 0
+    check(a)  # (the oracle refuses NaN codes anywhere in the cache)
+
+
 @pytest.mark.parametrize("hq,hkv", [(32, 1), (4, 4), (8, 2), (3, 1)])
 def test_attn_group_shapes(hq, hkv):
     a = wl.sparse_attn(rows=9, hq=hq, hkv=hkv, width=97, num_slots=700, seed=hq + 7 * hkv, short_every=3)
