@@ -944,24 +944,16 @@ struct ThrArgs {
 };
 
 // Two shapes of the threshold kernel.  Rows with many samples (long contexts): 1024-thread
-// workgroups that hold up to 15360 sample keys in LDS (60 KB; with the histogram two
-// workgroups fit on a CU), so the samples are read from memory once instead of once per
-// pass.  Rows with few samples: 256-thread workgroups without the LDS copy, many per CU.
-// Rows with more samples than the LDS copy holds read them from global memory on every pass.
-template <int NT, int STAGE>
-struct ThrStage {
-  uint32_t key[STAGE];
-};
-template <int NT>
-struct ThrStage<NT, 0> {
-  uint32_t key[1];
-};
-
+// workgroups whose threads keep their up to kThrStage / 1024 = 15 sample keys in registers
+// (every pass visits a thread's own samples j = thread + 1024 e), so the samples are read
+// from memory once instead of once per pass.  Rows with few samples: 256-thread workgroups,
+// many per CU.  Rows with more samples than the registers hold read them from global memory
+// on every pass.
 template <int kThrThreads, int kThrStage>
 __global__ __launch_bounds__(kThrThreads) void threshold_kernel(ThrArgs T) {
   __shared__ SelSmemT<64> sm;  // histogram and scan scratch only
-  __shared__ ThrStage<kThrThreads, kThrStage> stage;
-  uint32_t* skey = stage.key;
+  constexpr int PER = kThrStage > 0 ? (kThrStage + kThrThreads - 1) / kThrThreads : 1;
+  uint32_t kv[PER];  // this thread's sample keys j = thread + kThrThreads e (staged rows)
   const int r = blockIdx.x;
   if (r == 0 && threadIdx.x < kStatSlots) T.stats[threadIdx.x] = (threadIdx.x == kStatMin) ? 0x7FFFFFFF : 0;
   if (r == 0 && threadIdx.x < 2) T.fb_ctrl[threadIdx.x] = 0;
@@ -999,14 +991,12 @@ __global__ __launch_bounds__(kThrThreads) void threshold_kernel(ThrArgs T) {
       zero_hist<kThrThreads>(sm, kHistBins);
       __syncthreads();
       // The min/max pass reads the samples once; when they fit, their order keys stay in
-      // LDS for the two histogram passes.
+      // registers for the two histogram passes.
       const bool staged = n <= kThrStage;  // workgroup-uniform (never for kThrStage == 0)
       uint32_t lo = 0xFFFFFFFFu, hi = 0u;
       if constexpr (kThrStage > 0) {
         if (staged) {
           // Every load of the pass issued before any is used: one memory round trip.
-          constexpr int PER = (kThrStage + kThrThreads - 1) / kThrThreads;
-          uint32_t kv[PER];
 #pragma unroll
           for (int e = 0; e < PER; ++e) {
             const int j = (int)threadIdx.x + e * kThrThreads;
@@ -1014,9 +1004,7 @@ __global__ __launch_bounds__(kThrThreads) void threshold_kernel(ThrArgs T) {
           }
 #pragma unroll
           for (int e = 0; e < PER; ++e) {
-            const int j = (int)threadIdx.x + e * kThrThreads;
-            if (j < n) {
-              skey[j] = kv[e];
+            if ((int)threadIdx.x + e * kThrThreads < n) {
               lo = min(lo, kv[e]);
               hi = max(hi, kv[e]);
             }
@@ -1031,7 +1019,18 @@ __global__ __launch_bounds__(kThrThreads) void threshold_kernel(ThrArgs T) {
           hi = max(hi, k);
         }
       }
-      auto key_at = [&](int j) -> uint32_t { return staged ? skey[j] : order_key(sp[j]); };
+      // f(key) for each of this thread's samples
+      auto each_key = [&](auto&& f) __attribute__((always_inline)) {
+        if constexpr (kThrStage > 0) {
+          if (staged) {
+#pragma unroll
+            for (int e = 0; e < PER; ++e)
+              if ((int)threadIdx.x + e * kThrThreads < n) f(kv[e]);
+            return;
+          }
+        }
+        for (int j = threadIdx.x; j < n; j += kThrThreads) f(order_key(sp[j]));
+      };
       lo = wave_min_u32(lo);
       hi = wave_max_u32(hi);
       if (lane_id() == 0) {
@@ -1040,8 +1039,7 @@ __global__ __launch_bounds__(kThrThreads) void threshold_kernel(ThrArgs T) {
       }
       __syncthreads();
       const KeyNorm nz = key_norm(sm.kmin, sm.kmax);
-      for (int j = threadIdx.x; j < n; j += kThrThreads)
-        atomicAdd(&sm.hist[nz.normalize(key_at(j)) >> (32 - kHistBits)], 1u);
+      each_key([&](uint32_t key) { atomicAdd(&sm.hist[nz.normalize(key) >> (32 - kHistBits)], 1u); });
       __syncthreads();
       find_boundary<kThrThreads>(sm, kHistBins, (uint32_t)m);
       const uint32_t b1 = (uint32_t)sm.bnd_bin;
@@ -1049,10 +1047,10 @@ __global__ __launch_bounds__(kThrThreads) void threshold_kernel(ThrArgs T) {
       __syncthreads();
       zero_hist<kThrThreads>(sm, kHistBins);
       __syncthreads();
-      for (int j = threadIdx.x; j < n; j += kThrThreads) {
-        const uint32_t v = nz.normalize(key_at(j));
+      each_key([&](uint32_t key) {
+        const uint32_t v = nz.normalize(key);
         if ((v >> (32 - kHistBits)) == b1) atomicAdd(&sm.hist[(v >> (32 - 2 * kHistBits)) & (kHistBins - 1)], 1u);
-      }
+      });
       __syncthreads();
       find_boundary<kThrThreads>(sm, kHistBins, m2);
       const uint32_t v = (b1 << (32 - kHistBits)) | ((uint32_t)sm.bnd_bin << (32 - 2 * kHistBits));
