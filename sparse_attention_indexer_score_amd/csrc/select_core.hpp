@@ -560,7 +560,8 @@ __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out,
 #pragma unroll
     for (int u = 0; u < UV; ++u) cur[u] = nxt[u];
   }
-  // Scalar part: the rest (all of the row when it is not 16-byte aligned).
+  // Scalar part: the rest (all of the row when it is not 16-byte aligned), loads clamped
+  // like the vector part's.
   constexpr int U = 8;
   for (int base = nv * 4; base < n; base += U * NT) {
     uint32_t k_[U];
@@ -570,7 +571,7 @@ __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out,
     for (int u = 0; u < U; ++u) {
       const int j = base + u * NT + (int)threadIdx.x;
       ok[u] = j < n;
-      k_[u] = ok[u] ? order_key(x[j]) : 0u;
+      k_[u] = order_key(x[ok[u] ? j : n - 1]);
       ix_[u] = j;
     }
     append(k_, ok, ix_, std::integral_constant<int, U>{});
