@@ -56,6 +56,15 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
   return v;
 }
 
+// Workgroup barrier that orders LDS only: it waits for this wave's LDS operations, not for
+// its outstanding global loads (a full __syncthreads() also waits for those), so loads
+// issued ahead stay in flight across it.  Callers must not rely on it for global memory.
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Exclusive prefix sum over the threads of a workgroup of NT threads (thread order),
 // and the workgroup total.  `scratch` holds NT/64 + 1 words of LDS.  Contains barriers:
 // every thread of the workgroup must call it.
@@ -66,7 +75,7 @@ __device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t v, uint32_t* sc
   const int w = tid / kWave;
   const uint32_t inc = wave_inclusive_sum(v);
   if ((tid & (kWave - 1)) == kWave - 1) scratch[w] = inc;
-  __syncthreads();
+  lds_sync();
   if (tid == 0) {
     uint32_t run = 0;
     for (int i = 0; i < NW; ++i) {
@@ -76,10 +85,10 @@ __device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t v, uint32_t* sc
     }
     scratch[NW] = run;
   }
-  __syncthreads();
+  lds_sync();
   const uint32_t res = scratch[w] + inc - v;
   *total = scratch[NW];
-  __syncthreads();
+  lds_sync();
   return res;
 }
 

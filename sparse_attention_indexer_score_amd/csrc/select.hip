@@ -37,7 +37,11 @@ __global__ __launch_bounds__(kSelThreads, 8) void select_rows_kernel(const float
   if (m >= n) {
     for (int j = threadIdx.x; j < n; j += kSelThreads) o[j] = j;
   } else if (m > 0) {
-    block_select_sampled<kSelThreads>(x + off, n, m, o, sm);
+    const float* xr = x + off;
+    if ((reinterpret_cast<uintptr_t>(xr) & 15) == 0 && n >= 4)  // workgroup-uniform
+      block_select_sampled<kSelThreads, true>(xr, n, m, o, sm);
+    else
+      block_select_sampled<kSelThreads, false>(xr, n, m, o, sm);
   }
   for (int j = m + threadIdx.x; j < k; j += kSelThreads) o[j] = -1;
 }

@@ -137,7 +137,7 @@ __device__ void find_boundary(SM& sm, int nbins, uint32_t need) {
       above += c;
     }
   }
-  __syncthreads();
+  lds_sync();
 }
 
 // Wave-aggregated append: lanes with `pred` get consecutive slots from *counter.
@@ -174,7 +174,7 @@ __device__ void emit_at_least(const Src& src, int n, int shift, uint64_t prefix,
 // with zeroed, the caller has already cleared the first level's histogram.  Contains
 // barriers.
 template <int NT, class SM>
-__device__ void refine_lds(int L, uint32_t need, int32_t* out, SM& sm, const KeyNorm* nz1 = nullptr,
+__device__ __forceinline__ void refine_lds(int L, uint32_t need, int32_t* out, SM& sm, const KeyNorm* nz1 = nullptr,
                            bool zeroed = false) {
   constexpr int PER = (SM::kCap + NT - 1) / NT;
   for (bool first = true;; ++L, first = false) {
@@ -329,7 +329,7 @@ __device__ __forceinline__ void hist_level1(const Src& src, int n, SM& sm) {
 // Top-m of n elements (1 <= m <= n) by composite key; writes exactly m indices to
 // out[0..m) in unspecified order.  All NT threads must call it.  Contains barriers.
 template <int NT, class Src, class SM>
-__device__ void block_select(const Src& src, int n, int m, int32_t* out, SM& sm) {
+__device__ __forceinline__ void block_select(const Src& src, int n, int m, int32_t* out, SM& sm) {
   if (threadIdx.x == 0) {
     sm.nout = 0;
     sm.ntie = 0;
@@ -408,7 +408,7 @@ __device__ uint32_t block_kth_key(const Src& src, int n, int m, SM& sm, bool zer
     const int nbins = 1 << widths[L];
     if (!(L == 0 && zeroed)) {  // (zeroed: the caller cleared the first level's histogram)
       zero_hist<NT>(sm, nbins);
-      __syncthreads();
+      lds_sync();
     }
     for (int base = 0; base < n; base += NT) {
       const int j = base + (int)threadIdx.x;
@@ -418,11 +418,11 @@ __device__ uint32_t block_kth_key(const Src& src, int n, int m, SM& sm, bool zer
         if (match) atomicAdd(&sm.hist[(k >> sh) & (uint32_t)(nbins - 1)], 1u);
       }
     }
-    __syncthreads();
+    lds_sync();
     find_boundary<NT>(sm, nbins, need);
     const uint32_t b = (uint32_t)sm.bnd_bin;
     need -= sm.bnd_above;
-    __syncthreads();
+    lds_sync();
     prefix = (prefix << widths[L]) | b;
     above_shift = sh;
   }
@@ -445,7 +445,8 @@ __device__ uint32_t block_kth_key(const Src& src, int n, int m, SM& sm, bool zer
 // The result is exact either way; the sample only decides how much work is done.
 constexpr int kSelSamples = 2048;
 
-template <int NT, class SM>
+// VEC: x is 16-byte aligned and n >= 4 (the 16-byte path; otherwise the 4-byte path only).
+template <int NT, bool VEC, class SM>
 __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out, SM& sm) {
   static_assert(SM::kCap >= kSelSamples, "the sample lives in the candidate buffer");
   constexpr int SEG = 64, NSEG = kSelSamples / SEG;  // 32 runs of 64 consecutive keys
@@ -454,9 +455,8 @@ __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out,
   // issued before this step's keys are tested.  The first step's loads do not depend on
   // the threshold, so they are issued before the sample is taken and arrive under it.
   constexpr int UV = 4;
-  const bool vec = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
   const float4* xv = reinterpret_cast<const float4*>(x);
-  const int nv = vec ? n / 4 : 0;
+  const int nv = VEC ? n / 4 : 0;  // >= 1 with VEC
   float4 cur[UV], nxt[UV];
   // Unconditional loads (lanes past the end re-read the last vector and are masked when
   // tested): a load under a branch would leave the compiler unable to count the loads in
@@ -469,19 +469,32 @@ __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out,
       v[u] = xv[jv < nv ? jv : nv - 1];
     }
   };
-  if (nv > 0) load(cur, 0);
+  // The sample's loads go first: loads complete in order, so the sample can be ranked while
+  // the first step is still in flight (the barriers up to the streaming pass order LDS only).
+  constexpr int SPT = kSelSamples / NT;
+  static_assert(kSelSamples % NT == 0, "whole sample elements per thread");
+  float sv[SPT];
+  if (n > SM::kCap) {
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int t = i * NT + (int)threadIdx.x;
+      const int seg = t / SEG, e = t % SEG;
+      sv[i] = x[(int64_t)seg * (n - SEG) / (NSEG - 1) + e];
+    }
+  }
+  if constexpr (VEC) load(cur, 0);  // (unconditional, so that the sample's waits can be counted)
   uint32_t T = 0;
   if (threadIdx.x == 0) {
     sm.kmin = 0xFFFFFFFFu;
     sm.kmax = 0u;
   }
-  __syncthreads();
+  lds_sync();
   if (n > SM::kCap) {
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-    for (int t = threadIdx.x; t < kSelSamples; t += NT) {
-      const int seg = t / SEG, e = t % SEG;
-      const int64_t start = (int64_t)seg * (n - SEG) / (NSEG - 1);
-      const uint32_t k = order_key(x[start + e]);
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int t = i * NT + (int)threadIdx.x;
+      const uint32_t k = order_key(sv[i]);
       sm.tkey[t] = k;
       lo = min(lo, k);
       hi = max(hi, k);
@@ -493,13 +506,13 @@ __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out,
       atomicMax(&sm.kmax, hi);
     }
     zero_hist<NT>(sm, kHistBins);  // the sample's radix level, cleared under the same barrier
-    __syncthreads();
+    lds_sync();
     const KeyNorm nz = key_norm(sm.kmin, sm.kmax);
     int64_t rank = ((int64_t)7 * m * kSelSamples + (int64_t)4 * n - 1) / ((int64_t)4 * n);  // ceil(1.75 m S / n)
     rank = rank < 1 ? 1 : (rank > kSelSamples ? kSelSamples : rank);
     T = nz.denormalize(block_kth_key<NT, NormLdsKeySrc, SM, 1>(NormLdsKeySrc{sm.tkey, nz}, kSelSamples, (int)rank,
                                                                  sm, true));
-    __syncthreads();
+    lds_sync();
   }
   if (threadIdx.x == 0) {
     sm.ntie = 0;
@@ -507,7 +520,7 @@ __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out,
     sm.kmax = 0u;
   }
   zero_hist<NT>(sm, kHistBins);  // for the refinement (the streaming pass does not use it)
-  __syncthreads();
+  lds_sync();
   uint32_t kmax = 0u;
   // Appends the lanes' keys k_[u] (element ix_[u]) that pass, one LDS atomic per wave.
   auto append = [&](const uint32_t* k_, const bool* ok, const int* ix_, auto Uc) __attribute__((always_inline)) {
@@ -538,7 +551,7 @@ __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out,
     }
   };
   // Vector part: one append (one LDS atomic per wave) for all 4 * UV keys of a step.
-  for (int base = 0; base < nv; base += UV * NT) {
+  for (int base = 0; VEC && base < nv; base += UV * NT) {
     load(nxt, base + UV * NT);  // past the end on the last step: re-reads of the last vector
     uint32_t k_[4 * UV];
     bool ok[4 * UV];
