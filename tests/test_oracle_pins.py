@@ -2,13 +2,14 @@
 
 * exhaustive decode tables against torch's own fp8 / e8m0 / bf16 conversions and the
   OCP e2m1 value table;
-* the hand-worked fixtures under tests/golden (E1..E6);
+* the hand-worked fixtures under tests/golden (E1..E7, E7 = selected-value recall);
 * brute force in pure Python on tiny random inputs (decoded through torch, not the
   oracle's tables) with the top-k checked against its definition;
 * closed forms: one head with unit weight and non-negative inputs reduces the score to
   a plain dot product (torch float64 matmul); a power-of-two key scale scales every
   score exactly;
 * invariants of the selection on every workload family at reduced size;
+* per-row offsets of the selection-only entry against selection by rank counting;
 * planted mistakes: mutated copies of the oracle must fail at least one pin.
 """
 import math
@@ -463,3 +464,88 @@ def test_attn_grouped_heads_read_their_kv_head():
     for h in range(6):
         assert np.array_equal(out[0, h], vd[4, h // 2])
         assert not np.array_equal(out[0, h], vd[4, (h // 2 + 1) % 3])
+
+
+# ------------------------------------------------ selected-value recall and row offsets
+
+def _recall_cases():
+    from fractions import Fraction
+    g = golden("e7_selected_value_recall.json")
+    for row in g["rows"]:
+        x = np.array(row["x"], dtype=np.float32)
+        for c in row["cases"]:
+            yield x, np.array(c["idx"], dtype=np.int32), c["k"], float(Fraction(c["recall"]))
+
+
+def _recall_pins_pass(fn):
+    return all(math.isclose(fn(x, idx, k), want, abs_tol=1e-12) for x, idx, k, want in _recall_cases())
+
+
+def test_selected_value_recall_hand_worked():
+    """E7: recall values worked by hand, including a tie-broken index set with recall 1
+    and a repeated value counted with its multiplicity."""
+    for x, idx, k, want in _recall_cases():
+        assert math.isclose(oracle.selected_value_recall(x, idx, k), want, abs_tol=1e-12), (x, idx, k)
+
+
+def test_recall_pins_catch_planted_mistakes():
+    assert _recall_pins_pass(oracle.selected_value_recall)
+
+    def always_one(x, idx, k):
+        return 1.0
+
+    def index_sets(x, idx, k):
+        # compares index sets with the tie-broken top-k instead of value multisets
+        n = min(k, len(x))
+        ref = set(oracle.select_topk(x, k)[:n].tolist())
+        return len(ref & set(int(i) for i in idx if i >= 0)) / n if n else 1.0
+
+    def value_sets(x, idx, k):
+        # distinct values instead of multisets
+        n = min(k, len(x))
+        best = set(np.sort(x.astype(np.float64))[::-1][:n].tolist())
+        got = set(x[idx[idx >= 0]].astype(np.float64).tolist())
+        return len(best & got) / len(best) if n else 1.0
+
+    def over_k(x, idx, k):
+        # divides by k even when the row is shorter than k
+        r = oracle.selected_value_recall(x, idx, k)
+        return r * min(k, len(x)) / k
+
+    for bad in (always_one, index_sets, value_sets, over_k):
+        assert not _recall_pins_pass(bad), bad.__name__
+
+
+def _select_by_rank(v, k):
+    """Definition by counting: element j is kept iff fewer than k elements precede it in
+    the order (value descending, -0 == +0, lower index first)."""
+    v = [float(a) for a in v]
+    keep = []
+    for j in range(len(v)):
+        rank = sum(1 for i in range(len(v)) if v[i] > v[j] or (v[i] == v[j] and i < j))
+        if rank < k:
+            keep.append(j)
+    return sorted(keep)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_select_rows_row_start_brute_force(seed):
+    """select_rows with per-row offsets against selection by rank counting on the slice
+    x[r, row_start[r] : row_start[r] + length[r]], indices relative to the offset."""
+    rng = np.random.default_rng(100 + seed)
+    rows, ld, k = 6, 90, 11
+    x = rng.integers(-6, 7, size=(rows, ld)).astype(np.float32) * np.float32(0.25)  # dense ties
+    x[rng.random((rows, ld)) < 0.1] = np.float32(-0.0)
+    rs = rng.integers(0, ld, size=rows).astype(np.int32)
+    length = np.array([rng.integers(0, ld - s + 1) for s in rs], dtype=np.int32)
+    length[0] = 0                                                    # empty row
+    length[1] = min(5, ld - rs[1])                                   # shorter than k
+    got = oracle.select_rows(x, length, k, row_start=rs)
+    for r in range(rows):
+        v = x[r, rs[r]:rs[r] + length[r]]
+        want = _select_by_rank(v, k)
+        n = min(k, len(v))
+        assert sorted(got[r, :n].tolist()) == want, r
+        assert np.all(got[r, n:] == -1)
+    # the offsets matter: the same call without them differs on this input
+    assert not np.array_equal(oracle.select_rows(x, length, k), got)
