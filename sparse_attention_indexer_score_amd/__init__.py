@@ -31,7 +31,7 @@ _c_p = ctypes.c_void_p
 
 class IdxDebug(ctypes.Structure):
     _fields_ = [("cap", ctypes.c_int32), ("threshold_mode", ctypes.c_int32),
-                ("threshold_row_mod", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("threshold_row_mod", ctypes.c_int32), ("tie_cap", ctypes.c_int32)]
 
 
 class IdxProblem(ctypes.Structure):

@@ -259,7 +259,7 @@ int idx_sparse_attn(const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_
 
 size_t idx_score_workspace(const idx_problem* p) {
   if (check_problem(p, nullptr) != IDX_OK) return 0;
-  if (p->rows == 0) return 0;
+  if (p->rows == 0 || p->fmt != IDX_FMT_MXFP4) return 0;  // only the MXFP4 form keeps per-row pieces
   return lin_ws_bytes(p->rows);
 }
 
@@ -291,7 +291,8 @@ int idx_fused_topk(const idx_problem* p, int32_t k, int32_t* out_idx, void* ws, 
   if (k < 1 || k > IDX_MAX_TOPK) return IDX_EINVAL;
   if (p->rows > 0 && !out_idx) return IDX_EINVAL;
   if (!aligned(out_idx, 4)) return IDX_EALIGN;
-  if (p->debug && (p->debug->threshold_mode < 0 || p->debug->threshold_mode > 2 || p->debug->cap < 0))
+  if (p->debug && (p->debug->threshold_mode < 0 || p->debug->threshold_mode > 2 || p->debug->cap < 0 ||
+                   p->debug->tie_cap < 0 || p->debug->tie_cap > kTieCapHost))
     return IDX_EINVAL;
   const FusedSizes z = fused_sizes(p, k);
   if (stats) {
@@ -314,6 +315,7 @@ int idx_fused_topk(const idx_problem* p, int32_t k, int32_t* out_idx, void* ws, 
   F.fb_blocks = z.fb_blocks;
   F.debug_mode = p->debug ? p->debug->threshold_mode : 0;
   F.debug_row_mod = p->debug ? p->debug->threshold_row_mod : 0;
+  F.tie_cap = p->debug && p->debug->tie_cap > 0 ? p->debug->tie_cap : kTieCapHost;
   F.scratch_ld = z.scratch_ld;
   F.thr = reinterpret_cast<float*>(base + z.off_thr);
   F.cnt = reinterpret_cast<int32_t*>(base + z.off_cnt);

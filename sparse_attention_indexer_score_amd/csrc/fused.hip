@@ -26,6 +26,8 @@ namespace idx {
 
 enum : int { MODE_STORE = 0, MODE_FILTER = 1, MODE_SAMPLE = 2, MODE_ROWSTORE = 3 };
 
+static_assert(kTieCapHost == kTieCap, "host and device tie-buffer capacities differ");
+
 constexpr int kThreads = 256;  // 4 waves per workgroup
 constexpr int kTile = 32;      // keys per MFMA block
 
@@ -122,9 +124,22 @@ __device__ __forceinline__ int64_t map_item(const TileWork& W) {
   return W.total;  // not reached: the group's counts add up to nrb
 }
 
-// ============================================================================= contiguous K
+// ============================================================================= scoring core
 //
-// Main scoring core for contiguous keys.  Per (row, key):
+// Two forms of the head reduce, one per operand format.
+//
+// e4m3 (and paged e4m3) keys: score = kscale * sum_h w_h max(x_h, 0), each ReLU an integer
+// max on the bit pattern and each weighted term a VALU fma, in one fixed order per lane.
+// The fp8 MFMA does not sum its products exactly in fp32: within each group of 8 products,
+// terms far below the group's largest are dropped (measured: one 1.0 product with 2^-18
+// products beside it keeps only the 2^-18 terms of the other groups).  A linear term
+// computed on the matrix cores would carry that error in full, and cancelling it against
+// sum_h w_h |x_h| turns it into an error of the score itself (it is not bounded by the
+// score); the direct form has no such cancellation, and a key whose every head dot is
+// negative scores exactly 0.
+//
+// MXFP4 keys: e2m1 products span few binades, so the fp4 and fp6 MFMAs are exact, and the
+// ReLU is split to halve the VALU work.  Per (row, key):
 //
 //   score = kscale * 0.5 * (L + A),   A = sum_h w_h |x_h|,   L = sum_h w_h x_h,
 //
@@ -133,17 +148,24 @@ __device__ __forceinline__ int64_t map_item(const TileWork& W) {
 // L = u . k with u = sum_h w_h q_h, so it runs on the matrix cores.  u is split into
 // kPieces fp6 (e2m3) vectors with e8m0 block scales: each piece takes the top 4
 // significant bits of its block's largest residual, so the residual shrinks at least 16x
-// per piece (below 2^-20 of the block maximum after five; exact for integer u).  One extra
-// pair of MFMAs per tile multiplies up to three row pairs' pieces against the same key
+// per piece (below 2^-24 of the block maximum after six, the resolution of fp32 itself;
+// exact for integer u).  One extra pair of MFMAs per tile multiplies up to two row pairs'
+// pieces against the same key
 // operand; fp6 runs at the fp4 MFMA rate.  Every kernel that produces a
 // score for contiguous keys (materialised scores, samples, fused filter, fallback) runs
 // wg_tiles() below, so a (row, key) always gets the same instruction sequence, the same
 // MFMA row/column and the same summation order: the scores are bitwise identical.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-constexpr int kPieces = 5;
+constexpr int kPieces = 6;
 constexpr int kLinRowBytes = kPieces * 2 * 2 * 32;  // pieces x ksteps x halves x 32 bytes (24 used)
 constexpr int kLinRowScales = kPieces * 2 * 2;
+
+// The ReLU is split into a VALU |x| reduce and a linear MFMA tile (MXFP4 only).
+template <int FMT>
+struct SplitRelu {
+  static constexpr bool value = FMT == FMT_MXFP4;
+};
 
 // Rows per wave of the contiguous kernel: 4 for MXFP4 at 32 heads (the linear tile then
 // serves 4 rows and every key operand read from LDS feeds 8 MFMAs), otherwise 2 (register
@@ -237,7 +259,7 @@ __global__ __launch_bounds__(128) void lin_prep_kernel(const uint8_t* q, const u
         hh = h;
         pp = p;
       }
-  if (d < kPieces * 2 * 2 * 6) (&packed[0][0][0][0])[d] = 0;
+  for (int i = d; i < kPieces * 2 * 2 * 6; i += 128) (&packed[0][0][0][0])[i] = 0;
   float rd = u;
   for (int c = 0; c < kPieces; ++c) {
     res[ks * 64 + hh * 32 + pp] = fabsf(rd);
@@ -286,10 +308,10 @@ __device__ __forceinline__ void mfma_row(v16f (&acc)[H / 32], const RowOperand<F
   }
 }
 
-// Pieces of up to three row pairs of a wave as the A operand of the linear MFMA: lane l
-// supplies M row (l % 32) = 8g + 4hh + j, slot s = 4g + j holds piece (s % 5) of row
-// row0 + 2 (s / 5) + hh.  In the result, lane half H then holds in accumulator s the
-// piece dot products of row row0 + 2 (s / 5) + H, the row its head sums land on.
+// Pieces of up to two row pairs of a wave as the A operand of the linear MFMA: lane l
+// supplies M row (l % 32) = 8g + 4hh + j, slot s = 4g + j holds piece (s % kPieces) of row
+// row0 + 2 (s / kPieces) + hh.  In the result, lane half H then holds in accumulator s the
+// piece dot products of row row0 + 2 (s / kPieces) + H, the row its head sums land on.
 struct LinOperand {
   v8i a[2];
   int sa;  // block scales of the two K-steps, byte ks
@@ -343,6 +365,20 @@ __device__ __forceinline__ float lin_of_pair(const v16f& a, int p) {
 __device__ __forceinline__ float finish_score2(float abs_sum, float lin, float half_kscale) {
   return (lin + abs_sum) * half_kscale;
 }
+
+// The score as it is stored, appended or sampled: clamped at +0.  A sum of ReLU terms is
+// never negative, but the split form can round a score whose exact value is 0 (every head
+// dot <= 0) to a tiny negative number.  Integer max on the bit pattern: -0.0 and negative
+// values become +0.0.  The filter compares unclamped scores against thresholds that are
+// either > 0 or -inf, for which both forms give the same answer.
+__device__ __forceinline__ float clamp0(float x) {
+  const int b = __float_as_int(x);
+  return __int_as_float(b > 0 ? b : 0);
+}
+
+// max(x, 0) of a head dot in the direct form: an integer max on the bit pattern (one VALU
+// instruction, no NaN canonicalisation; -0.0 becomes +0.0).
+__device__ __forceinline__ float relu_bits(float x) { return clamp0(x); }
 
 // Key tiles are staged through LDS: all four waves of a workgroup use the same keys, so a
 // stage of 32-key tiles is fetched once per workgroup with 16-byte loads straight into LDS
@@ -417,6 +453,8 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
       } else {
         plo[i] = ks;
         phi[i] = ke;
+        // stored scores stay inside the caller's row pitch whatever the device-side range
+        if (MODE == MODE_STORE && (int64_t)ke - ks > E.ld) phi[i] = ks + (int)E.ld;
       }
     }
     if (phi[i] > plo[i]) {
@@ -432,8 +470,9 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
 #pragma unroll
   for (int i = 0; i < RW; ++i)
     if (row0 + i < A.rows) load_row<FMT, H>(ro[i], A, row0 + i);
+  constexpr bool kSplit = SplitRelu<FMT>::value;
   LinOperand lo;
-  load_lin(lo, L, row0, A.rows, NP);
+  if constexpr (kSplit) load_lin(lo, L, row0, A.rows, NP);
 
   float thr_l[NP];
 #pragma unroll
@@ -549,7 +588,7 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
           if ((m[p] >> l) & 1) {
             const int slot = (half ? ccnt[2 * p + 1] - nA : ccnt[2 * p]) + mask_prefix(m[p]);
             const int o = (2 * p + half) * kCandBuf + slot;
-            cs[o] = score_of[p];
+            cs[o] = clamp0(score_of[p]);
             ci[o] = (int32_t)(key - lane_pair(ksr, p));
           }
           ccnt[2 * p] += nA;
@@ -562,7 +601,7 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
     } else {
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const float score = score_of[p];
+        const float score = clamp0(score_of[p]);
         const bool valid = full || (pos >= lane_pair(plo, p) && pos < lane_pair(phi, p));
         if constexpr (MODE == MODE_STORE) {
           if (valid) E.out[row_of(p) * E.ld + (key - lane_pair(ksr, p))] = score;
@@ -618,22 +657,29 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
       ko.sb = 0x7F7F7F7F;
     }
     // Read unconditionally and select (no branch per tile); without key scales the LDS
-    // word is never written and its value is discarded.
+    // word is never written and its value is discarded.  The split form takes half the
+    // scale (it finishes (L + A) / 2).
     const float kv = *reinterpret_cast<const __attribute__((address_space(3))) float*>(sb.ks + i * kTile * 4);
-    half_kscale = A.k_scale ? 0.5f * kv : 0.5f;
+    if constexpr (kSplit) half_kscale = A.k_scale ? 0.5f * kv : 0.5f;
+    else half_kscale = A.k_scale ? kv : 1.0f;
   };
   struct Acc {
     v16f row[RW][H / 32];
     v16f lin;
   };
   auto issue = [&](Acc& a, const KeyOperand& ko) {
-    a.lin = mfma_lin<FMT>(lo, ko);
+    if constexpr (kSplit) a.lin = mfma_lin<FMT>(lo, ko);
 #pragma unroll
     for (int r = 0; r < RW; ++r) mfma_row<FMT, H>(a.row[r], ro[r], ko);
   };
   // Head reduce of all RW rows; at 4 rows per wave the rows' chains are interleaved for
   // instruction-level parallelism.  Each row's own sum runs over its heads in one fixed order.
-  auto reduce = [&](const Acc& a, float half_kscale, float* sc) {
+  // term(x): |x| (split form) or max(x, 0) (direct form).
+  auto term = [](float x) -> float {
+    if constexpr (kSplit) return __builtin_fabsf(x);
+    else return relu_bits(x);
+  };
+  auto reduce = [&](const Acc& a, float kscale_f, float* sc) {
     float part[RW];
 #pragma unroll
     for (int r = 0; r < RW; ++r) part[r] = 0.0f;
@@ -644,7 +690,7 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
         for (int i = 0; i < 16; ++i)
 #pragma unroll
           for (int r = 0; r < RW; ++r)
-            part[r] = __builtin_fmaf(ro[r].w[mt][i], __builtin_fabsf(a.row[r][mt][i]), part[r]);
+            part[r] = __builtin_fmaf(ro[r].w[mt][i], term(a.row[r][mt][i]), part[r]);
     } else {  // same sums, row after row (fewer live registers)
 #pragma unroll
       for (int r = 0; r < RW; ++r)
@@ -652,11 +698,14 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
         for (int mt = 0; mt < H / 32; ++mt)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            part[r] = __builtin_fmaf(ro[r].w[mt][i], __builtin_fabsf(a.row[r][mt][i]), part[r]);
+            part[r] = __builtin_fmaf(ro[r].w[mt][i], term(a.row[r][mt][i]), part[r]);
     }
 #pragma unroll
-    for (int p = 0; p < NP; ++p)
-      sc[p] = finish_score2(combine_halves(part[2 * p], part[2 * p + 1]), lin_of_pair(a.lin, p), half_kscale);
+    for (int p = 0; p < NP; ++p) {
+      const float hs = combine_halves(part[2 * p], part[2 * p + 1]);
+      if constexpr (kSplit) sc[p] = finish_score2(hs, lin_of_pair(a.lin, p), kscale_f);
+      else sc[p] = hs * kscale_f;
+    }
   };
   // One tile: key operand from LDS, MFMAs for all RW rows and the linear tile, reduce, epilogue.
   auto compute = [&](const StageBase& sb, int i, int t, bool known_full) {
@@ -1055,6 +1104,9 @@ __global__ __launch_bounds__(kThrThreads) void threshold_kernel(ThrArgs T) {
       find_boundary<kThrThreads>(sm, kHistBins, m2);
       const uint32_t v = (b1 << (32 - kHistBits)) | ((uint32_t)sm.bnd_bin << (32 - 2 * kHistBits));
       tr = order_key_to_float(nz.denormalize(v));
+      // Sample scores are clamped at +0, so tr >= 0; tr == 0 keeps every key (and the slab
+      // overflows into the fallback) — as -inf, which the filter's unclamped compare needs.
+      if (!(tr > 0.0f)) tr = -__builtin_inff();
     }
   }
   if (threadIdx.x == 0) T.thr[r] = tr;
@@ -1072,7 +1124,7 @@ struct SlabArgs {
   long long* stats;
   int32_t* fb_ctrl;
   int32_t* fb_list;
-  int32_t k, cap, want_stats;
+  int32_t k, cap, want_stats, tie_cap;
 };
 
 // Candidates of a slab row with keys normalised over the row's [min, max] candidate key:
@@ -1094,7 +1146,7 @@ constexpr int kSlabThreads = 512;
 __global__ __launch_bounds__(kSlabThreads) void slab_select_kernel(SlabArgs S) {
   __shared__ SelSmem sm;
   const int r = blockIdx.x;
-  const int V = S.ke[r] - S.ks[r];
+  const int V = max(S.ke[r] - S.ks[r], 0);  // (an invalid range ke < ks counts as empty)
   const int c = S.cnt[r];
   const int need = min(S.k, V);
   int32_t* out = S.out + (int64_t)r * S.k;
@@ -1143,7 +1195,7 @@ __global__ __launch_bounds__(kSlabThreads) void slab_select_kernel(SlabArgs S) {
       atomicMax(&sm.kmax, hi);
     }
     __syncthreads();
-    block_select<kSlabThreads>(NormPairSrc{ss, si, key_norm(sm.kmin, sm.kmax)}, c, need, out, sm);
+    block_select<kSlabThreads>(NormPairSrc{ss, si, key_norm(sm.kmin, sm.kmax)}, c, need, out, sm, S.tie_cap);
   }
   for (int j = need + threadIdx.x; j < S.k; j += kSlabThreads) out[j] = -1;
 }
@@ -1156,7 +1208,7 @@ struct FbArgs {
   float* scratch;
   int64_t scratch_ld;
   int32_t* out;
-  int32_t k;
+  int32_t k, tie_cap;
 };
 
 
@@ -1183,7 +1235,7 @@ __global__ __launch_bounds__(kThreads) void fallback_tiles_kernel(ScoreArgs A, L
     if (item >= F.fb_ctrl[0]) break;  // every wave sees the same item and count
     const int r = F.fb_list[item];
     const int ks = A.ks[r], ke = A.ke[r];
-    const int V = ke - ks;
+    const int V = max(ke - ks, 0);
     if (V > 0) {
       EpiArgs E = {};
       E.out = mine;
@@ -1195,7 +1247,7 @@ __global__ __launch_bounds__(kThreads) void fallback_tiles_kernel(ScoreArgs A, L
     __syncthreads();
     const int need = min(F.k, V);
     int32_t* out = F.out + (int64_t)r * F.k;
-    if (need > 0) block_select<kThreads>(RowSrc{mine}, V, need, out, sm);
+    if (need > 0) block_select<kThreads>(RowSrc{mine}, V, need, out, sm, F.tie_cap);
     for (int j = need + threadIdx.x; j < F.k; j += kThreads) out[j] = -1;
     __syncthreads();
   }
@@ -1317,11 +1369,14 @@ void lin_carve(void* ws, int32_t rows, uint8_t** q8, uint8_t** sf) {
 
 hipError_t launch_score_store(const DevProblem& P, float* out, int64_t ld, void* ws, hipStream_t s) {
   if (P.rows == 0) return hipSuccess;
-  uint8_t *q8, *sf;
-  lin_carve(ws, P.rows, &q8, &sf);
-  hipError_t e = launch_lin_prep(P, q8, sf, s);
-  if (e != hipSuccess) return e;
-  const LinArgs L{q8, sf};
+  LinArgs L{nullptr, nullptr};
+  if (P.fmt == FMT_MXFP4) {  // the split form's per-row pieces
+    uint8_t *q8, *sf;
+    lin_carve(ws, P.rows, &q8, &sf);
+    hipError_t e = launch_lin_prep(P, q8, sf, s);
+    if (e != hipSuccess) return e;
+    L = LinArgs{q8, sf};
+  }
   EpiArgs E = {};
   E.out = out;
   E.ld = ld;
@@ -1334,7 +1389,7 @@ hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_id
   auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
   if ((e = mark(0)) != hipSuccess) return e;
   const LinArgs L = lin_args(F);
-  if ((e = launch_lin_prep(P, F.lin_q8, F.lin_sf, s)) != hipSuccess) return e;
+  if (P.fmt == FMT_MXFP4 && (e = launch_lin_prep(P, F.lin_q8, F.lin_sf, s)) != hipSuccess) return e;
   // K1a: samples
   {
     EpiArgs E = {};
@@ -1399,6 +1454,7 @@ hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_id
     S.k = F.k;
     S.cap = F.cap;
     S.want_stats = F.want_stats;
+    S.tie_cap = F.tie_cap;
     slab_select_kernel<<<dim3(P.rows), dim3(kSlabThreads), 0, s>>>(S);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(4)) != hipSuccess) return e;
@@ -1413,6 +1469,7 @@ hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_id
     B.scratch_ld = F.scratch_ld;
     B.out = out_idx;
     B.k = F.k;
+    B.tie_cap = F.tie_cap;
     const dim3 grid(F.fb_blocks), block(kThreads);
     if (P.fmt == FMT_E4M3) {  // contiguous or paged
       if (P.heads == 64) fallback_tiles_kernel<FMT_E4M3, 64><<<grid, block, 0, s>>>(A, L, B);

@@ -28,6 +28,7 @@ struct DevProblem {
 struct FusedPlan {
   int32_t k, cap, stride, ns, fb_blocks;
   int32_t debug_mode, debug_row_mod;
+  int32_t tie_cap;  // tie-buffer capacity of the slab select and the fallback (<= kTieCap)
   int64_t scratch_ld;
   // workspace regions
   float* thr;
@@ -43,6 +44,9 @@ struct FusedPlan {
   uint8_t* lin_q8;  // pieces of sum_h w_h q_h (contiguous keys)
   uint8_t* lin_sf;
 };
+
+// Tie-buffer capacity of the selection (host copy of the device constant kTieCap).
+constexpr int kTieCapHost = 4096;
 
 enum StatSlot { kStatStoreAll = 0, kStatSampled, kStatFallback, kStatMax, kStatMin, kStatTotal, kStatSlots = 8 };
 

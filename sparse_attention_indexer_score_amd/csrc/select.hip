@@ -25,14 +25,28 @@ constexpr int kSelThreads = 1024;
 // a CU.
 constexpr int kSelCand = 6144;
 
+// Row r's elements: n = len[r] values from offset row_start[r] of the row, clamped into
+// [0, ld) whatever the device-side values are, so that reads stay inside the row and the
+// padding writes inside out[r][0, k); m = min(k, n).  Returns the element offset of the
+// row's first value.
+__device__ __forceinline__ int64_t row_span(int64_t ld, const int32_t* row_start, const int32_t* len, int r, int k,
+                                            int& n, int& m) {
+  int64_t rs = row_start ? row_start[r] : 0;
+  rs = rs < 0 ? 0 : (rs > ld ? ld : rs);
+  int64_t nn = len[r];
+  nn = nn < 0 ? 0 : (nn > ld - rs ? ld - rs : nn);
+  n = (int)nn;
+  m = min(k, n);
+  return (int64_t)r * ld + rs;
+}
+
 __global__ __launch_bounds__(kSelThreads, 8) void select_rows_kernel(const float* x, int64_t ld,
                                                                   const int32_t* row_start, const int32_t* len,
                                                                   int32_t k, int32_t* out) {
   __shared__ SelSmemT<kSelCand> sm;
   const int r = blockIdx.x;
-  const int n = len[r];
-  const int64_t off = (int64_t)r * ld + (row_start ? row_start[r] : 0);
-  const int m = min(k, n);
+  int n, m;
+  const int64_t off = row_span(ld, row_start, len, r, k, n, m);
   int32_t* o = out + (int64_t)r * k;
   if (m >= n) {
     for (int j = threadIdx.x; j < n; j += kSelThreads) o[j] = j;
@@ -93,14 +107,14 @@ __global__ __launch_bounds__(kSelThreads) void mb_hist_kernel(const float* x, in
                                                               const int32_t* len, int32_t k, int32_t g, SplitWs W) {
   __shared__ SelSmem sm;
   const int r = blockIdx.x / g, part = blockIdx.x % g;
-  const int n = len[r];
-  if (min(k, n) >= n) return;  // the refine kernel writes trivial rows
+  int n, m;
+  const int64_t row_off = row_span(ld, row_start, len, r, k, n, m);
+  if (m >= n) return;  // the refine kernel writes trivial rows
   int lo, hi;
   segment(n, g, part, lo, hi);
   zero_hist<kSelThreads>(sm, kHistBins);
   __syncthreads();
-  const int64_t off = (int64_t)r * ld + (row_start ? row_start[r] : 0) + lo;
-  hist_level1<kSelThreads>(RowSrc{x + off}, hi - lo, sm);
+  hist_level1<kSelThreads>(RowSrc{x + row_off + lo}, hi - lo, sm);
   __syncthreads();
   uint32_t* gh = W.hist + (int64_t)r * kHistBins;
   for (int b = threadIdx.x; b < kHistBins; b += kSelThreads)
@@ -124,8 +138,8 @@ __global__ __launch_bounds__(kSelThreads) void mb_scatter_kernel(const float* x,
   __shared__ SelSmem sm;
   __shared__ int32_t eidx[kMaxTopK];
   const int r = blockIdx.x / g, part = blockIdx.x % g;
-  const int n = len[r];
-  const int m = min(k, n);
+  int n, m;
+  const int64_t off = row_span(ld, row_start, len, r, k, n, m);
   if (m >= n) return;
   load_row_hist(sm, W.hist + (int64_t)r * kHistBins);
   find_boundary<kSelThreads>(sm, kHistBins, (uint32_t)m);
@@ -140,7 +154,6 @@ __global__ __launch_bounds__(kSelThreads) void mb_scatter_kernel(const float* x,
   __syncthreads();
   int lo, hi;
   segment(n, g, part, lo, hi);
-  const int64_t off = (int64_t)r * ld + (row_start ? row_start[r] : 0);
   const int l = lane_id();
   // U elements per thread and step, loaded unconditionally at clamped positions (a load under
   // a branch is waited for before the next is issued); lanes past the end are masked.
@@ -194,10 +207,9 @@ __global__ __launch_bounds__(kSelThreads) void mb_refine_kernel(const float* x, 
                                                                 int32_t k, int32_t* out, SplitWs W) {
   __shared__ SelSmem sm;
   const int r = blockIdx.x;
-  const int n = len[r];
-  const int m = min(k, n);
+  int n, m;
+  const int64_t off = row_span(ld, row_start, len, r, k, n, m);
   int32_t* o = out + (int64_t)r * k;
-  const int64_t off = (int64_t)r * ld + (row_start ? row_start[r] : 0);
   if (m >= n) {
     for (int j = threadIdx.x; j < n; j += kSelThreads) o[j] = j;
   } else {

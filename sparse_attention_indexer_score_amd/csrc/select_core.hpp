@@ -327,9 +327,12 @@ __device__ __forceinline__ void hist_level1(const Src& src, int n, SM& sm) {
 }
 
 // Top-m of n elements (1 <= m <= n) by composite key; writes exactly m indices to
-// out[0..m) in unspecified order.  All NT threads must call it.  Contains barriers.
+// out[0..m) in unspecified order.  A boundary bin of more than tie_cap (<= SM::kCap)
+// elements is resolved by rescanning the input.  All NT threads must call it.  Contains
+// barriers.
 template <int NT, class Src, class SM>
-__device__ __forceinline__ void block_select(const Src& src, int n, int m, int32_t* out, SM& sm) {
+__device__ __forceinline__ void block_select(const Src& src, int n, int m, int32_t* out, SM& sm,
+                                             int tie_cap = SM::kCap) {
   if (threadIdx.x == 0) {
     sm.nout = 0;
     sm.ntie = 0;
@@ -355,7 +358,7 @@ __device__ __forceinline__ void block_select(const Src& src, int n, int m, int32
     __syncthreads();
     return;
   }
-  if (cnt <= (uint32_t)SM::kCap) {
+  if (cnt <= (uint32_t)tie_cap) {
     // U elements per thread and step, loaded unconditionally (clamped; the extra lanes are
     // masked), so that a step's loads are in flight together.
     constexpr int U = 4;

@@ -70,3 +70,31 @@ def check_topk_invariants(x, sel, k):
     tie_rest = np.nonzero(~mask & (x == vmin))[0]
     if len(tie_rest):
         assert tie_sel.max() < tie_rest.min(), "ties must go to the lower key index"
+
+
+def negative_dot_problem(fmt="e4m3", rows=24, num_keys=3000, heads=64, sigma=1.0, w_hi=1.0 / 64,
+                         kscale=(0.5, 2.0), frac_neg=0.5, topk=512, seed=0):
+    """Rows whose query heads share a common direction v (q_h = sigma (v + 0.3 z_h)), and keys
+    of which a fraction frac_neg point against it (k = sigma (-v + 0.3 z')): for those keys
+    every head dot is strongly negative, so their exact score is 0, while the others are
+    N(0, sigma^2).  Returns (problem, bool mask [num_keys] of the planted keys).  Causal ranges
+    over the whole key array; w ~ U(0, w_hi); kscale ~ U(kscale) (None: no key scale; e4m3
+    only)."""
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal(wl.HEAD_DIM).astype(np.float32)
+    q = sigma * (v[None, None, :] + 0.3 * rng.standard_normal((rows, heads, wl.HEAD_DIM)).astype(np.float32))
+    neg = rng.random(num_keys) < frac_neg
+    k = sigma * rng.standard_normal((num_keys, wl.HEAD_DIM)).astype(np.float32)
+    k[neg] = sigma * (-v[None, :] + 0.3 * rng.standard_normal((int(neg.sum()), wl.HEAD_DIM)).astype(np.float32))
+    w = wl.encode_bf16(rng.uniform(0.0, w_hi, size=(rows, heads)))
+    ks = np.zeros(rows, dtype=np.int32)
+    ke = (num_keys - rows + 1 + np.arange(rows)).astype(np.int32)
+    if fmt == "e4m3":
+        ksc = None if kscale is None else rng.uniform(*kscale, size=num_keys).astype(np.float32)
+        p = wl.Problem("negdot", wl.FMT_E4M3, rows, heads, wl.encode_e4m3(q), None, wl.encode_e4m3(k), None,
+                       ksc, w, ks, ke, topk, num_keys)
+    else:
+        qp, qs = wl.encode_mxfp4(q)
+        kp, kss = wl.encode_mxfp4(k)
+        p = wl.Problem("negdot", wl.FMT_MXFP4, rows, heads, qp, qs, kp, kss, None, w, ks, ke, topk, num_keys)
+    return p, neg

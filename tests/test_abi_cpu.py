@@ -121,16 +121,18 @@ def test_fused_argument_checks():
 
 def test_score_workspace_and_check():
     lib = sai.library()
-    p = _problem(rows=64, num_keys=4096)
+    assert lib.idx_score_workspace(ctypes.byref(_problem(rows=64, num_keys=4096))) == 0   # e4m3: none
+    sf = ctypes.c_void_p(0x20000)
+    p = _problem(rows=64, num_keys=4096, fmt=sai.IDX_FMT_MXFP4, q_sf=sf, k_sf=sf)
     need = lib.idx_score_workspace(ctypes.byref(p))
-    assert need >= 64 * 660
+    assert need >= 64 * 780                          # six fp6 pieces of u per row, and their scales
     out = ctypes.c_void_p(0x40000)
     assert lib.idx_score(ctypes.byref(p), out, 4096, None, 0, None) == sai.IDX_EWS
     assert lib.idx_score(ctypes.byref(p), out, 4096, ctypes.c_void_p(0x100000), need - 1, None) == sai.IDX_EWS
     assert lib.idx_score(ctypes.byref(p), out, 4096, ctypes.c_void_p(0x100080), need, None) == sai.IDX_EALIGN
     paged = _problem(rows=4, page_table=ctypes.c_void_p(0x30000), row_req=ctypes.c_void_p(0x30000), num_req=1,
                      max_pages=2, num_keys=128)
-    assert lib.idx_score_workspace(ctypes.byref(paged)) >= 4 * 660   # linear-tile pieces of every row
+    assert lib.idx_score_workspace(ctypes.byref(paged)) == 0        # paged keys are e4m3
 
 
 def test_fused_workspace_grows_with_k_and_cap():
@@ -200,3 +202,26 @@ def test_sparse_attn_argument_checks():
     assert f(kc=ctypes.c_void_p(0x10004)) == sai.IDX_EALIGN
     assert f(out=ctypes.c_void_p(0x10002)) == sai.IDX_EALIGN
     assert f(rows=0, q=None, kc=None, vc=None, sl=None, out=None) == 0   # nothing to do
+
+
+def test_debug_hooks_are_validated_on_the_host():
+    """Out-of-range debug overrides are rejected before any device work (tie_cap within
+    1..4096, 0 = default; threshold_mode 0..2; cap >= 0)."""
+    lib = sai.library()
+    p = _problem(rows=4, num_keys=1000)
+    out = ctypes.c_void_p(0x40000)
+    ws = ctypes.c_void_p(0x100000)
+    for dbg in (IdxDebug(tie_cap=-1), IdxDebug(tie_cap=4097), IdxDebug(threshold_mode=3), IdxDebug(cap=-5)):
+        p.debug = ctypes.pointer(dbg)
+        assert lib.idx_fused_topk(ctypes.byref(p), 64, out, ws, 1 << 30, None, None) == sai.IDX_EINVAL
+
+
+def test_split_gate_of_the_workloads():
+    """Row split on 256 CUs: the selection workload (64 rows of pitch 131072) gets g = 4;
+    the decode batch (512 rows) and the prefill batch (4096 rows of 65536) get 256 / rows < 4
+    workgroups per row, so the split is off; 8 rows split 32 ways once a row reaches 65536."""
+    assert sai.idx_row_split(64, 131072, 256) == 4
+    assert sai.idx_row_split(512, 262144, 256) == 0
+    assert sai.idx_row_split(4096, 65536, 256) == 0
+    assert sai.idx_row_split(8, 65535, 256) == 0
+    assert sai.idx_row_split(8, 65536, 256) == 32

@@ -44,13 +44,19 @@ def assert_same_sets(a, b, what=""):
 
 def check_scores_close(p, sc, rows):
     kd = oracle.all_keys(p) if p.page_table is None else None
+    worst = 0.0
     for r in rows:
         V = int(p.ke[r] - p.ks[r])
         ref = oracle.row_scores(p, r, kd_all=kd).astype(np.float64)
         got = sc[r, :V].astype(np.float64)
         err = np.abs(got - ref)
         lim = ATOL + RTOL * np.abs(ref)
+        if V:
+            worst = max(worst, float((err / lim).max()))
         assert np.all(err <= lim), f"row {r}: max err {err.max():.3g} at {int(np.argmax(err - lim))}"
+    print(f"[scores] {p.name} ({p.fmt}, H={p.heads}): max |err| / (1e-4 + 1e-5 |oracle|) = {worst:.3g} "
+          f"over {len(list(rows))} rows", flush=True)
+    return worst
 
 
 def full_check(p, k, score_rows=None, fused_kw=None):
@@ -197,7 +203,8 @@ def test_fused_k_range_ragged_mxfp4(k):
 
 
 def test_edge_lengths_e4m3():
-    """Empty rows, V < k, V == k, V == cap, V == cap + 1 and full rows; k = 512, cap = 2048."""
+    """Empty rows, V < k, V > k, V == cap, V == cap + 1 and full rows, with offset starts;
+    k = 512, cap = 2048 (V == k exactly: test_gpu_rare_paths.py)."""
     p = wl.tiny(rows=12, num_keys=4096, topk=512, seed=5)
     ke = np.array([0, 1, 7, 511, 512, 513, 2048, 2049, 3000, 4095, 4096, 4096], dtype=np.int32)
     ks = np.array([0, 0, 3, 0, 100, 0, 0, 0, 1000, 0, 0, 37], dtype=np.int32)
@@ -293,22 +300,7 @@ def test_select_row_start_offsets():
     assert_same_sets(got, ref)
 
 
-# ----------------------------------------------------------------------------- forced fallback
-
-@pytest.mark.parametrize("mode,row_mod,cap", [(1, 0, 0), (2, 0, 0), (1, 3, 0), (0, 0, 512), (2, 5, 1500)])
-def test_forced_fallback_matches(mode, row_mod, cap):
-    p = wl.prefill(rows=40, num_keys=5000, topk=256, seed=8)
-    dp = dev(p)
-    dp.debug = sai.IdxDebug(cap=cap, threshold_mode=mode, threshold_row_mod=row_mod)
-    sc, V = gpu_scores(dp, p)
-    ref = oracle.select_rows(sc, V, 256)
-    got, st = sai.idx_fused_topk(dp, 256, stats=True)
-    assert_same_sets(got.cpu().numpy(), ref, "forced")
-    capv = cap if cap > 0 else 1024
-    forced = [r for r in range(p.rows) if mode and (row_mod <= 0 or r % row_mod == 0)]
-    expect_min = sum(1 for r in forced if (mode == 1 and V[r] > 0) or (mode == 2 and V[r] > capv))
-    assert st["fallback_rows"] >= expect_min
-
+# ----------------------------------------------------------------------------- determinism
 
 def test_fused_is_deterministic():
     p = wl.long_context(rows=32, num_keys=20000, band_keys=3000, topk=1024, seed=17)
