@@ -43,6 +43,8 @@ extern "C" {
 #define IDX_EWS (-4)    /* workspace smaller than the *_workspace query returned */
 #define IDX_EHIP (-5)   /* a HIP runtime call or kernel launch failed */
 #define IDX_ENODEV (-6) /* no usable gfx950 device is current */
+#define IDX_ESCRATCH (-7) /* the problem needs more workspace than the library's fixed scratch
+                             (idx_fused_topk_noalloc) */
 
 /* ------------------------------------------------------------------ limits */
 #define IDX_HEAD_DIM 128  /* head_dim of q and k */
@@ -209,6 +211,20 @@ int idx_fused_topk(const idx_problem* p, int32_t k, int32_t* out_idx, void* ws, 
 /* Bytes of workspace idx_fused_topk needs for this problem shape and k (host only;
  * reads only the scalar fields of p).  Returns 0 for invalid arguments.            */
 size_t idx_fused_workspace(const idx_problem* p, int32_t k);
+
+/* idx_fused_topk_noalloc — idx_fused_topk for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the workspace is a fixed device array inside the library, IDX_NOALLOC_SCRATCH_BYTES per
+ * GPU it runs on, held until the process ends.  The caller still passes the inputs and
+ * out_idx.  The call itself allocates nothing (its first call on a device resolves that
+ * device's copy of the array).  Problems whose idx_fused_workspace(p, k) exceeds the
+ * array return IDX_ESCRATCH (the decode/MTP batch of 512 rows over 256K-token contexts at
+ * k = 2048 needs about 72 MiB; 4096 prefill rows of 64K keys need about 282 MiB and do
+ * not fit).  All calls on one GPU share its array: calls that overlap on one GPU (other
+ * streams or threads) race and must be serialised by the caller.  It reports no
+ * statistics (no host read-back); the result is identical to idx_fused_topk's.      */
+#define IDX_NOALLOC_SCRATCH_BYTES (128u << 20)
+int idx_fused_topk_noalloc(const idx_problem* p, int32_t k, int32_t* out_idx, void* stream);
 
 /* ------------------------------------------------------------------ paged output
  * idx_page_slots — selected logical positions to physical KV slots for a paged cache

@@ -22,7 +22,8 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libidx.so")
 
-IDX_OK, IDX_EINVAL, IDX_EFMT, IDX_EALIGN, IDX_EWS, IDX_EHIP, IDX_ENODEV = 0, -1, -2, -3, -4, -5, -6
+IDX_OK, IDX_EINVAL, IDX_EFMT, IDX_EALIGN, IDX_EWS, IDX_EHIP, IDX_ENODEV, IDX_ESCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
+IDX_NOALLOC_SCRATCH_BYTES = 128 << 20
 IDX_FMT_E4M3, IDX_FMT_MXFP4 = 1, 2
 IDX_HEAD_DIM, IDX_MAX_TOPK, IDX_PAGE = 128, 2048, 64
 
@@ -79,6 +80,7 @@ def _lib():
             "idx_select_workspace": (sz, [i32, i64, i32]),
             "idx_fused_topk": (ctypes.c_int, [P, i32, _c_p, _c_p, sz, ctypes.POINTER(IdxStats), _c_p]),
             "idx_fused_workspace": (sz, [P, i32]),
+            "idx_fused_topk_noalloc": (ctypes.c_int, [P, i32, _c_p, _c_p]),
             "idx_page_slots": (ctypes.c_int, [_c_p, i32, i32, _c_p, _c_p, _c_p, i32, _c_p, _c_p]),
             "idx_sparse_attn": (ctypes.c_int, [_c_p, _c_p, _c_p, i64, _c_p, i32, i32, i32, i32, ctypes.c_float,
                                                ctypes.c_float, _c_p, _c_p]),
@@ -315,6 +317,17 @@ def idx_fused_topk(prob: DeviceProblem, k: int, stats: bool = False, stream=None
     """Exact top-k without materialising scores.  Returns out [rows, k] (and a stats dict)."""
     out, st = FusedRunner(prob, k)(stats=stats, stream=stream)
     return (out, st) if stats else out
+
+
+def idx_fused_topk_noalloc(prob: DeviceProblem, k: int, out: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """idx_fused_topk on the library's fixed scratch (no workspace argument).  out: int32
+    [rows, k] (allocated here when not given)."""
+    if out is None:
+        out = torch.empty((prob.rows, k), dtype=torch.int32, device=prob.device)
+    s = prob.struct()
+    _check(_lib().idx_fused_topk_noalloc(ctypes.byref(s), k, _ptr(out), _stream(stream)), "idx_fused_topk_noalloc")
+    return out
 
 
 def idx_page_slots(idx: torch.Tensor, page_table: torch.Tensor, row_req: torch.Tensor,

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libidx.so")
 
-SOURCES = ["capi.cpp", "fused.hip", "select.hip", "slots.hip", "attn.hip"]
+SOURCES = ["capi.cpp", "fused.hip", "select.hip", "slots.hip", "attn.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

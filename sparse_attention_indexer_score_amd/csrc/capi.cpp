@@ -177,6 +177,7 @@ const char* idx_strerror(int code) {
     case IDX_EWS: return "workspace too small";
     case IDX_EHIP: return "HIP runtime or kernel launch error";
     case IDX_ENODEV: return "no gfx950 device is current";
+    case IDX_ESCRATCH: return "problem needs more workspace than the library's fixed scratch";
     default: return "unknown error";
   }
 }

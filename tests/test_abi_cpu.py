@@ -225,3 +225,16 @@ def test_split_gate_of_the_workloads():
     assert sai.idx_row_split(4096, 65536, 256) == 0
     assert sai.idx_row_split(8, 65535, 256) == 0
     assert sai.idx_row_split(8, 65536, 256) == 32
+
+
+def test_noalloc_checks_on_the_host():
+    """idx_fused_topk_noalloc validates like idx_fused_topk and rejects problems whose
+    workspace exceeds the fixed scratch before any device work."""
+    lib = sai.library()
+    out = ctypes.c_void_p(0x40000)
+    assert lib.idx_fused_topk_noalloc(ctypes.byref(_problem(heads=48)), 64, out, None) == sai.IDX_EINVAL
+    assert lib.idx_fused_topk_noalloc(ctypes.byref(_problem()), 0, out, None) == sai.IDX_EINVAL
+    big = _problem(rows=4096, num_keys=65536, heads=64)
+    assert lib.idx_fused_workspace(ctypes.byref(big), 2048) > sai.IDX_NOALLOC_SCRATCH_BYTES
+    assert lib.idx_fused_topk_noalloc(ctypes.byref(big), 2048, out, None) == sai.IDX_ESCRATCH
+    assert b"scratch" in lib.idx_strerror(sai.IDX_ESCRATCH)
