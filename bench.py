@@ -60,28 +60,44 @@ def load_traffic(workload, launch_bytes_alg):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(p, rows_sample):
-    """The oracle as it stands, timed on the host cores over a bounded sample of rows."""
-    import oracle
+def cpu_threads():
+    """Host threads for the CPU baseline: the process's CPU share, at most 16 (one GPU's share
+    of a GPU machine)."""
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(p, rows_sample):
+    """The oracle as it stands, timed on the host cores over a bounded sample of rows: one
+    oracle call (scores of the row's visible keys, then the full sort) per row, rows spread
+    over a pool of threads, each running single-threaded BLAS (NumPy releases the GIL in the
+    matmul and the sort).  One decode of K is included."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    threads = cpu_threads()
     t0 = time.perf_counter()
-    oracle.topk(p, rows=rows_sample)
+    with threadpool_limits(1):
+        kd = oracle.all_keys(p) if p.page_table is None else None
+        one = lambda r: oracle.select_topk(oracle.row_scores(p, r, kd_all=kd), p.topk)
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(one, rows_sample))
     dt = time.perf_counter() - t0
     pairs = int(sum(int(p.ke[r]) - int(p.ks[r]) for r in rows_sample))
-    return {"value": pairs / dt / 1e9, "unit": "Gkey-scores/s", "cores": int(cores), "kind": "oracle",
+    return {"value": pairs / dt / 1e9, "unit": "Gkey-scores/s", "cores": threads, "kind": "oracle",
+            "host_cpus": os.cpu_count(),
             "sample": f"{len(rows_sample)} of {p.rows} rows (every {p.rows // len(rows_sample)}th), all their "
-                      f"visible keys ({pairs} key-scores), scoring + full sort; includes one decode of K; "
-                      f"{dt:.1f} s"}
+                      f"visible keys ({pairs} key-scores), scoring + full sort per row, rows over {threads} "
+                      f"threads with single-threaded BLAS; includes one decode of K; {dt:.1f} s"}
 
 
-def timed_ms(fn, iters, flush=None):
-    """Median and minimum HIP-event time of fn() on torch's current stream (the stream the
-    library launches on when given none).  flush() runs between iterations, outside the
-    timed region."""
+def step_ms(fn, iters, flush=None):
+    """Sorted per-call HIP-event times (ms) of fn() on torch's current stream (the stream the
+    library launches on when given none); flush() runs before every call, outside its
+    events."""
     import torch
     marks = []
     for _ in range(iters):
@@ -93,22 +109,76 @@ def timed_ms(fn, iters, flush=None):
         e1.record()
         marks.append((e0, e1))
     torch.cuda.synchronize()
-    ms = sorted(a.elapsed_time(b) for a, b in marks)
+    return sorted(a.elapsed_time(b) for a, b in marks)
+
+
+def timed_ms(fn, iters, flush=None):
+    """Median and minimum of step_ms."""
+    ms = step_ms(fn, iters, flush)
     return ms[len(ms) // 2], ms[0]
 
 
-def secondary_legs(dev, iters=20):
-    """Selection (HBM-bound) and materialised scoring, measured beside the fused path:
-    idx_select on the selection workload (64 rows, pitch 131072) and on the prefill
-    workload's materialised scores (4096 x 65536 fp32, 1.04 GB), idx_score on prefill, and
-    the consumer, idx_sparse_attn (512 rows x 2048 selected slots; HBM-bound gather).
-    Cold numbers flush L2 and the 256 MB MALL with a 512 MiB fill before every call."""
+def stage_pass(runner, iters, flush):
+    """Per-stage HIP-event times of iters fused calls (recorded by the library on its launch
+    stream), each preceded by the cache flush as in the timed steps: mean per stage."""
+    import torch
+    import sparse_attention_indexer_score_amd as sai
+    sai.idx_timing_enable(iters)
+    for _ in range(iters):
+        flush()
+        runner()
+    torch.cuda.synchronize()
+    rec = sai.idx_timing_read(iters)
+    sai.idx_timing_disable()
+    return {s: float(np.mean([c[s] for c in rec])) for s in sai.FUSED_STAGES}
+
+
+def fused_leg(p, dev, iters, flush, what):
+    """Fused top-k on one workload: cold per-call time (median, minimum), stage split and the
+    score + filter kernel against the MFMA peak of the workload's format."""
+    import torch
+    import sparse_attention_indexer_score_amd as sai
+    dp = sai.DeviceProblem.from_host(p, dev)
+    runner = sai.FusedRunner(dp, p.topk)
+    _, st = runner(stats=True)
+    runner()
+    torch.cuda.synchronize()
+    ms = step_ms(runner, iters, flush)
+    stages = stage_pass(runner, iters, flush)
+    med = ms[len(ms) // 2]
+    alg = p.pairs * 2 * 128 * p.heads
+    k2 = stages["score_filter"]
+    res = {"what": what, "ms": round(med, 4), "min_ms": round(ms[0], 4),
+           "Gkey_scores_per_s": round(p.pairs / (med * 1e-3) / 1e9, 2),
+           "score_filter_ms": round(k2, 4), "score_filter_TFLOPs": round(alg / (k2 * 1e-3) / 1e12, 1),
+           "score_filter_frac": round(alg / (k2 * 1e-3) / 1e12 / PEAK_TFLOPS[p.fmt], 4),
+           "peak_TFLOPs": PEAK_TFLOPS[p.fmt], "stage_ms": {s: round(v, 4) for s, v in stages.items()},
+           "fallback_rows": st["fallback_rows"]}
+    del runner, dp
+    torch.cuda.empty_cache()
+    return res
+
+
+def secondary_legs(dev, iters=20, main_workload="long"):
+    """Measured beside the headline: the fused top-k on the other two fused workloads
+    (long / prefill / decode), selection (HBM-bound) and materialised scoring: idx_select on
+    the selection workload (64 rows, pitch 131072) and on the prefill workload's materialised
+    scores (4096 x 65536 fp32, 1.04 GB), idx_score on prefill, and the consumer,
+    idx_sparse_attn (512 rows x 2048 selected slots; HBM-bound gather).  Cold numbers flush L2
+    and the 256 MB MALL with a 512 MiB fill before every call."""
     import torch
     import sparse_attention_indexer_score_amd as sai
     from sparse_attention_indexer_score_amd import workloads as wl
     flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     flush = lambda: flush_buf.fill_(0x5A)
     res = {}
+
+    for w in ("long", "prefill", "decode"):
+        if w == main_workload:
+            continue
+        log(f"[bench] fused top-k on the {w} workload")
+        res[f"fused_{w}"] = fused_leg(wl.make(w), dev, iters, flush, WORKLOADS[w])
+        log(f"[bench] fused {w}: {res[f'fused_{w}']['ms']} ms, K2 {res[f'fused_{w}']['score_filter_frac']} of peak")
 
     sp = wl.make("select")
     x = torch.from_numpy(sp.x).to(dev)
@@ -214,7 +284,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long", choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-rows", type=int, default=96, help="rows in the oracle's timed sample (0: skip)")
+    ap.add_argument("--cpu-rows", type=int, default=512, help="rows in the oracle's timed sample (0: skip)")
     ap.add_argument("--routing", action="store_true",
                     help="only measure dense (idx_score + idx_select) against fused top-k over context lengths")
     ap.add_argument("--no-secondary", action="store_true",
@@ -269,23 +339,23 @@ def main():
         runner()
     torch.cuda.synchronize()
 
-    sai.idx_timing_enable(args.steps)
-    stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Timed steps: before each, a 512 MiB fill evicts the inputs from L2 and the 256 MB MALL
+    # (outside the step's events); each step is bracketed by HIP events on the launch stream.
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = lambda: flush_buf.fill_(0x5A)
     torch.cuda.synchronize()
-    ev0.record(stream)
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        runner()
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    ms_steps = step_ms(runner, args.steps, flush)
     wall = time.perf_counter() - t0
-    stages = sai.idx_timing_read(args.steps)
-    sai.idx_timing_disable()
-    ms = ev0.elapsed_time(ev1) / args.steps
-    log(f"[bench] {args.steps} steps: {ms:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f} ms/step)")
+    ms = ms_steps[len(ms_steps) // 2]
+    log(f"[bench] {args.steps} steps: median {ms:.3f} ms, min {ms_steps[0]:.3f} ms, mean "
+        f"{float(np.mean(ms_steps)):.3f} ms (wall {wall * 1e3 / args.steps:.3f} ms/step incl. flushes)")
+    warm_ms = float(np.mean(step_ms(runner, args.steps)))
+    # Stage split from a separate pass of the same flushed steps (the library's own events on
+    # its launch stream), so that the timed steps record nothing but their own two events.
+    stage_ms = stage_pass(runner, args.steps, flush)
+    log(f"[bench] stages: {stage_ms}")
 
-    stage_ms = {s: float(np.mean([c[s] for c in stages])) for s in sai.FUSED_STAGES}
     pairs = p.pairs
     value = pairs / (ms * 1e-3) / 1e9
     flops_per_pair = 2 * 128 * p.heads
@@ -294,8 +364,9 @@ def main():
     achieved = alg_flops / (k2_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[p.fmt]
     traffic = load_traffic(args.workload, None)
+    del flush_buf
 
-    secondary = None if args.no_secondary else secondary_legs(dev)
+    secondary = None if args.no_secondary else secondary_legs(dev, main_workload=args.workload)
 
     cpu = None
     if args.cpu_rows > 0:
@@ -314,6 +385,9 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "fused_topk_ms": round(ms, 4),
+        "fused_topk_min_ms": round(ms_steps[0], 4),
+        "fused_topk_warm_ms": round(warm_ms, 4),
+        "timing": "median of the timed steps, each cold (L2 and MALL flushed by a 512 MiB fill before it)",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
