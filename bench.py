@@ -202,7 +202,7 @@ def secondary_legs(dev, iters=20, main_workload="long"):
     sr = sai.ScoreRunner(dpp, ld=int((pp.ke - pp.ks).max()))
     sr()
     torch.cuda.synchronize()
-    s_med, s_min = timed_ms(sr, 10)
+    s_med, s_min = timed_ms(sr, min(10, iters))
     pairs = pp.pairs
     res["score_prefill"] = {
         "what": "idx_score, prefill workload (4096 x 65536, e4m3, 64 heads): fp32 scores written",
@@ -289,6 +289,8 @@ def main():
                     help="only measure dense (idx_score + idx_select) against fused top-k over context lengths")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the selection and materialised-score measurements")
+    ap.add_argument("--secondary-iters", type=int, default=20,
+                    help="timed calls per secondary leg (fewer for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for HBM counters)")
     args = ap.parse_args()
@@ -366,7 +368,8 @@ def main():
     traffic = load_traffic(args.workload, None)
     del flush_buf
 
-    secondary = None if args.no_secondary else secondary_legs(dev, main_workload=args.workload)
+    secondary = None if args.no_secondary else secondary_legs(dev, iters=args.secondary_iters,
+                                                              main_workload=args.workload)
 
     cpu = None
     if args.cpu_rows > 0:
