@@ -250,32 +250,80 @@ def secondary_legs(dev, iters=20, main_workload="long"):
     return res
 
 
-def routing_table(dev, rows=2048, contexts=(4096, 8192, 16384, 32768, 65536, 131072), k=2048, iters=10):
-    """Dense path (idx_score writes every score, idx_select reads them back) against the fused
-    path on the prefill family (e4m3, 64 heads, causal) at a fixed batch and growing context,
-    to locate the crossover.  Returns one record per context length."""
+def flush_cold(dev):
+    """A 512 MiB fill that evicts L2 and the MALL (the flush between cold calls)."""
+    import torch
+    buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    return lambda: buf.fill_(0x5A)
+
+
+def dense_runner(dp, p):
+    """The dense route: idx_score writes every visible score as fp32 [rows, max V], then
+    idx_select reads them back (preallocated buffers, nothing allocated per call)."""
+    import torch
+    import sparse_attention_indexer_score_amd as sai
+    sr = sai.ScoreRunner(dp, ld=int((p.ke - p.ks).max()))
+    sel = sai.SelectRunner(sr.out, (dp.ke - dp.ks).to(torch.int32), p.topk)
+    return (lambda: (sr(), sel())), sr, sel
+
+
+def dense_leg(p, dp, dev, iters, flush, fused_ms):
+    """Dense route on the given problem (cold calls, median and minimum) against the fused
+    median: the logits the fused path never writes are written and read back here."""
+    import torch
+    run, sr, sel = dense_runner(dp, p)
+    run()
+    torch.cuda.synchronize()
+    med, mn = timed_ms(run, iters, flush)
+    res = {"what": "dense route on the same problem: idx_score writes fp32 [rows, max V], idx_select reads it",
+           "ms": round(med, 4), "min_ms": round(mn, 4), "logits_bytes": int(p.pairs) * 4,
+           "fused_ms": round(fused_ms, 4), "fused_over_dense_speedup": round(med / fused_ms, 3)}
+    del run, sr, sel
+    torch.cuda.empty_cache()
+    return res
+
+
+ROUTING = {
+    # family: (generator, rows list, key counts)
+    "prefill_e4m3_64h": ("prefill", (512, 2048, 4096), (4096, 8192, 16384, 32768, 65536, 131072)),
+    "long_mxfp4_32h": ("long", (512, 2048, 4096), (16384, 65536, 262144, 1048576)),
+}
+
+
+def routing_table(dev, families=None, k=2048, iters=5):
+    """Dense route (idx_score + idx_select) against the fused top-k per format, batch and
+    context length (causal rows, every call cold), and the crossover per batch: the shortest
+    context at which the fused path is faster."""
     import torch
     import sparse_attention_indexer_score_amd as sai
     from sparse_attention_indexer_score_amd import workloads as wl
-    out = []
-    for n in contexts:
-        p = wl.prefill(rows=rows, num_keys=n, topk=k, seed=3)
-        dp = sai.DeviceProblem.from_host(p, dev)
-        fused = sai.FusedRunner(dp, k)
-        sr = sai.ScoreRunner(dp, ld=int((p.ke - p.ks).max()))
-        sel = sai.SelectRunner(sr.out, (dp.ke - dp.ks).to(torch.int32), k)
-        dense = lambda: (sr(), sel())
-        fused(); dense()
-        torch.cuda.synchronize()
-        f_ms, _ = timed_ms(fused, iters)
-        d_ms, _ = timed_ms(dense, iters)
-        rec = {"keys": n, "rows": rows, "pairs": int(p.pairs), "fused_ms": round(f_ms, 4), "dense_ms": round(d_ms, 4),
-               "fused_over_dense_speedup": round(d_ms / f_ms, 3)}
-        log(f"[routing] {rec}")
-        out.append(rec)
-        del fused, sr, sel, dp
-        torch.cuda.empty_cache()
-    return out
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = lambda: flush_buf.fill_(0x5A)
+    table, crossover = [], {}
+    for fam in (families or ROUTING):
+        gen, rows_list, keys_list = ROUTING[fam]
+        for rows in rows_list:
+            cross = None
+            for n in keys_list:
+                if n < rows:
+                    continue
+                p = wl.make(gen, rows=rows, num_keys=n, topk=k)
+                dp = sai.DeviceProblem.from_host(p, dev)
+                fused = sai.FusedRunner(dp, k)
+                fused()
+                torch.cuda.synchronize()
+                f_ms, _ = timed_ms(fused, iters, flush)
+                d = dense_leg(p, dp, dev, iters, flush, f_ms)
+                rec = {"family": fam, "rows": rows, "keys": n, "pairs": int(p.pairs), "fused_ms": round(f_ms, 4),
+                       "dense_ms": d["ms"], "fused_over_dense_speedup": d["fused_over_dense_speedup"]}
+                log(f"[routing] {rec}")
+                table.append(rec)
+                if cross is None and d["fused_over_dense_speedup"] > 1.0:
+                    cross = n
+                del fused, dp, p
+                torch.cuda.empty_cache()
+            crossover[f"{fam}/rows={rows}"] = cross
+    return table, crossover
 
 
 def main():
@@ -307,10 +355,11 @@ def main():
     if args.routing:
         dev = torch.device("cuda:0")
         torch.cuda.set_device(dev)
-        table = routing_table(dev)
-        print(json.dumps({"metric": "fused vs dense indexer top-k ms by context length (prefill family, 2048 rows, "
-                                    "e4m3, 64 heads, k=2048), 1 GPU", "n_gpus": 1, "data": "synthetic",
-                          "higher_is_better": False, "table": table}), flush=True)
+        table, crossover = routing_table(dev)
+        print(json.dumps({"metric": "fused vs dense indexer top-k ms by format, batch and context length (causal, "
+                                    "k=2048, every call cold), 1 GPU", "n_gpus": 1, "data": "synthetic",
+                          "higher_is_better": False, "table": table,
+                          "crossover_keys": crossover}), flush=True)
         return
 
     log(f"[bench] generating workload '{args.workload}'")
@@ -368,8 +417,12 @@ def main():
     traffic = load_traffic(args.workload, None)
     del flush_buf
 
-    secondary = None if args.no_secondary else secondary_legs(dev, iters=args.secondary_iters,
-                                                              main_workload=args.workload)
+    secondary = None
+    if not args.no_secondary:
+        dense = dense_leg(p, dp, dev, min(5, args.steps), flush_cold(dev), ms)
+        log(f"[bench] dense route on the same problem: {dense['ms']} ms (fused {ms:.3f} ms)")
+        secondary = {"dense_route": dense}
+        secondary.update(secondary_legs(dev, iters=args.secondary_iters, main_workload=args.workload))
 
     cpu = None
     if args.cpu_rows > 0:
