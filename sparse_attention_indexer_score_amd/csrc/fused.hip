@@ -141,11 +141,12 @@ __device__ __forceinline__ int64_t map_item(const TileWork& W) {
 // MXFP4 keys: e2m1 products span few binades, so the fp4 and fp6 MFMAs are exact, and the
 // ReLU is split to halve the VALU work.  Per (row, key):
 //
-//   score = kscale * 0.5 * (L + A),   A = sum_h w_h |x_h|,   L = sum_h w_h x_h,
+//   score = kscale * (L + A),   A = sum_h (w_h / 2) |x_h|,   L = sum_h (w_h / 2) x_h,
 //
-// which equals kscale * sum_h w_h max(x_h, 0) because max(x, 0) = (x + |x|) / 2.  A costs
-// one VALU fma (abs source modifier) per head in the head reduce.  L is linear in the key:
-// L = u . k with u = sum_h w_h q_h, so it runs on the matrix cores.  u is split into
+// which equals kscale * sum_h w_h max(x_h, 0) because max(x, 0) = (x + |x|) / 2 (the 1/2
+// rides on w, exactly).  A costs one VALU fma (abs source modifier) per head in the head
+// reduce.  L is linear in the key: L = u . k with u = sum_h (w_h / 2) q_h, so it runs on
+// the matrix cores.  u is split into
 // kPieces fp6 (e2m3) vectors with e8m0 block scales: each piece takes the top 4
 // significant bits of its block's largest residual, so the residual shrinks at least 16x
 // per piece (below 2^-24 of the block maximum after six, the resolution of fp32 itself;
@@ -160,12 +161,6 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 constexpr int kPieces = 6;
 constexpr int kLinRowBytes = kPieces * 2 * 2 * 32;  // pieces x ksteps x halves x 32 bytes (24 used)
 constexpr int kLinRowScales = kPieces * 2 * 2;
-
-// The ReLU is split into a VALU |x| reduce and a linear MFMA tile (MXFP4 only).
-template <int FMT>
-struct SplitRelu {
-  static constexpr bool value = FMT == FMT_MXFP4;
-};
 
 // Rows per wave of the contiguous kernel: 4 for MXFP4 at 32 heads (the linear tile then
 // serves 4 rows and every key operand read from LDS feeds 8 MFMAs), otherwise 2 (register
@@ -250,6 +245,7 @@ __global__ __launch_bounds__(128) void lin_prep_kernel(const uint8_t* q, const u
     }
     u = __builtin_fmaf(bf16_to_f32(w[hv]), qd, u);
   }
+  u *= 0.5f;  // the split form's 1/2 (exact)
   // Where element d sits in the pieces: kstep, lane half (= scale block) and position.
   const int ks = d / 64, e = d % 64;
   int hh = 0, pp = 0;
@@ -308,10 +304,14 @@ __device__ __forceinline__ void mfma_row(v16f (&acc)[H / 32], const RowOperand<F
   }
 }
 
-// Pieces of up to two row pairs of a wave as the A operand of the linear MFMA: lane l
-// supplies M row (l % 32) = 8g + 4hh + j, slot s = 4g + j holds piece (s % kPieces) of row
-// row0 + 2 (s / kPieces) + hh.  In the result, lane half H then holds in accumulator s the
-// piece dot products of row row0 + 2 (s / kPieces) + H, the row its head sums land on.
+// Pieces of up to two row pairs of a wave as the A operand of the linear MFMA.  Lane l
+// supplies M row (l % 32) = 8g + 4hh + j, which lands in accumulator s = 4g + j of lane
+// half hh.  With p = s / kPieces and c = s % kPieces, accumulator s holds
+//   c = 0: piece hh of row 2p      (the start value of row 2p's head sum, both halves),
+//   c = 1: piece hh of row 2p + 1  (the start value of row 2p + 1's head sum),
+//   c >= 2: piece c of row 2p + hh (the row whose score lane half hh receives after the
+//           half-wave combine, added then),
+// rows counted from row0.  So each row's six pieces reach its score with four adds.
 struct LinOperand {
   v8i a[2];
   int sa;  // block scales of the two K-steps, byte ks
@@ -360,12 +360,6 @@ __device__ __forceinline__ float lin_of_pair(const v16f& a, int p) {
   return x;
 }
 
-// score = kscale * (lin + abs_sum) / 2, given half_kscale = kscale / 2 (exact: a power-of-two
-// factor moves freely between the two products while nothing underflows).
-__device__ __forceinline__ float finish_score2(float abs_sum, float lin, float half_kscale) {
-  return (lin + abs_sum) * half_kscale;
-}
-
 // The score as it is stored, appended or sampled: clamped at +0.  A sum of ReLU terms is
 // never negative, but the split form can round a score whose exact value is 0 (every head
 // dot <= 0) to a tiny negative number.  Integer max on the bit pattern: -0.0 and negative
@@ -399,7 +393,7 @@ template <int FMT>
 struct StageLds {
   uint8_t* codes;  // [2][kKeys * kStride]
   uint32_t* sf;    // [2][kKeys] e8m0 words (MXFP4)
-  float* ks;       // [2][kKeys] half the per-key scale (0.5 when absent)
+  float* ks;       // [2][kKeys] per-key scale (1.0 when absent)
   float* cand_s;   // FILTER: [waves][RW][kCandBuf] candidate scores of this workgroup's rows
   int32_t* cand_i; //         and their key indices relative to ks
   int32_t* pages;  // paged: kPageCache page ids of the call's key range (nullptr: read the table)
@@ -424,7 +418,7 @@ constexpr int kCandBuf = 256;
 // selects the rows that count (the others see no keys); req >= 0 reads keys through
 // request req's page table, clamped to klim when given (else to this wave's rows' last
 // visible key).  MODE_ROWSTORE writes only row E.only_row, to E.out[key - ks].
-template <int FMT, int H, int MODE, int RW, bool SHARED>
+template <int FMT, int H, int MODE, int RW, bool SHARED, bool KS = true>
 __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, const EpiArgs& E, int row0,
                                          int phase, int S, int c0, int c1, int tA, int tB,
                                          const StageLds<FMT>& sl, int req = -1, uint32_t rmask = ~0u,
@@ -635,7 +629,7 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
                      opaque(sl.sf + buf * G::kKeys + col), opaque(sl.ks + buf * G::kKeys + col)};
   };
   // Key operand and half key scale of tile slot i of the stage at `sb`.
-  auto read_b = [&](const StageBase& sb, int i, KeyOperand& ko, float& half_kscale) {
+  auto read_b = [&](const StageBase& sb, int i, KeyOperand& ko, float& kscale) {
     lds_ptr row = sb.codes + i * kTile * G::kStride;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -656,12 +650,8 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
     } else {
       ko.sb = 0x7F7F7F7F;
     }
-    // Read unconditionally and select (no branch per tile); without key scales the LDS
-    // word is never written and its value is discarded.  The split form takes half the
-    // scale (it finishes (L + A) / 2).
-    const float kv = *reinterpret_cast<const __attribute__((address_space(3))) float*>(sb.ks + i * kTile * 4);
-    if constexpr (kSplit) half_kscale = A.k_scale ? 0.5f * kv : 0.5f;
-    else half_kscale = A.k_scale ? kv : 1.0f;
+    // Without key scales the LDS words hold 1.0 (written once, before the first stage).
+    kscale = *reinterpret_cast<const __attribute__((address_space(3))) float*>(sb.ks + i * kTile * 4);
   };
   struct Acc {
     v16f row[RW][H / 32];
@@ -703,8 +693,9 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const float hs = combine_halves(part[2 * p], part[2 * p + 1]);
-      if constexpr (kSplit) sc[p] = finish_score2(hs, lin_of_pair(a.lin, p), kscale_f);
-      else sc[p] = hs * kscale_f;
+      // KS = false: no key scales (every factor 1.0, so the product is skipped, not changed)
+      if constexpr (kSplit) sc[p] = KS ? (lin_of_pair(a.lin, p) + hs) * kscale_f : lin_of_pair(a.lin, p) + hs;
+      else sc[p] = KS ? hs * kscale_f : hs;
     }
   };
   // One tile: key operand from LDS, MFMAs for all RW rows and the linear tile, reduce, epilogue.
@@ -799,6 +790,8 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
   };
 
   const int nst = (tB - tA + G::kTiles - 1) / G::kTiles;
+  if (!has_ks)  // workgroup-uniform: key scale 1.0 in both stage buffers (no load writes them)
+    for (int j = threadIdx.x; j < 2 * G::kKeys; j += kThreads) sl.ks[j] = 1.0f;
   dma(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -869,7 +862,7 @@ struct CandShared<RW, false> {
   int32_t i[1];
 };
 
-template <int FMT, int H, int MODE>
+template <int FMT, int H, int MODE, bool KS>
 __global__ __launch_bounds__(kThreads, 2) void score_tiles_kernel(ScoreArgs A, LinArgs L, EpiArgs E, TileWork W) {
   constexpr int RW = RowsPerWave<FMT, H>::value;
   __shared__ StageShared<FMT> sh;
@@ -899,7 +892,7 @@ __global__ __launch_bounds__(kThreads, 2) void score_tiles_kernel(ScoreArgs A, L
   const int tA = max(c0, lo) / kTile, tB = (min(c1, hi) + kTile - 1) / kTile;
   if (tA >= tB) return;  // workgroup-uniform
   const StageLds<FMT> sl{sh.codes, sh.sf, sh.ks, cand.s, cand.i};
-  wg_tiles<FMT, H, MODE, RW, false>(A, L, E, rb * 4 * RW + wave * RW, phase, S, c0, c1, tA, tB, sl);
+  wg_tiles<FMT, H, MODE, RW, false, KS>(A, L, E, rb * 4 * RW + wave * RW, phase, S, c0, c1, tA, tB, sl);
 }
 
 // Request of a paged row, clamped to [0, num_req) so an invalid id cannot read outside
@@ -1316,11 +1309,17 @@ static hipError_t dispatch_score(const DevProblem& P, const LinArgs& L, const Ep
     if (P.heads == 64) score_pages_kernel<FMT_E4M3, 64, MODE><<<grid, block, 0, s>>>(A, L, E, W);
     else score_pages_kernel<FMT_E4M3, 32, MODE><<<grid, block, 0, s>>>(A, L, E, W);
   } else if (P.fmt == FMT_E4M3) {
-    if (P.heads == 64) score_tiles_kernel<FMT_E4M3, 64, MODE><<<grid, block, 0, s>>>(A, L, E, W);
-    else score_tiles_kernel<FMT_E4M3, 32, MODE><<<grid, block, 0, s>>>(A, L, E, W);
+    if (P.heads == 64) score_tiles_kernel<FMT_E4M3, 64, MODE, true><<<grid, block, 0, s>>>(A, L, E, W);
+    else score_tiles_kernel<FMT_E4M3, 32, MODE, true><<<grid, block, 0, s>>>(A, L, E, W);
   } else {
-    if (P.heads == 64) score_tiles_kernel<FMT_MXFP4, 64, MODE><<<grid, block, 0, s>>>(A, L, E, W);
-    else score_tiles_kernel<FMT_MXFP4, 32, MODE><<<grid, block, 0, s>>>(A, L, E, W);
+    const bool ks = A.k_scale != nullptr;  // MXFP4 keys usually come without per-key scales
+    if (P.heads == 64) {
+      if (ks) score_tiles_kernel<FMT_MXFP4, 64, MODE, true><<<grid, block, 0, s>>>(A, L, E, W);
+      else score_tiles_kernel<FMT_MXFP4, 64, MODE, false><<<grid, block, 0, s>>>(A, L, E, W);
+    } else {
+      if (ks) score_tiles_kernel<FMT_MXFP4, 32, MODE, true><<<grid, block, 0, s>>>(A, L, E, W);
+      else score_tiles_kernel<FMT_MXFP4, 32, MODE, false><<<grid, block, 0, s>>>(A, L, E, W);
+    }
   }
   return hipGetLastError();
 }

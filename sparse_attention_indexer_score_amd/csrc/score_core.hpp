@@ -55,13 +55,21 @@ struct ScoreArgs {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// MXFP4 scores use the split form of the ReLU (a VALU |x| reduce plus a linear MFMA tile,
+// whose sum is twice the score); its factor 1/2 is carried by w here and by the linear
+// tile's vector u, both halved exactly (a power of two).
+template <int FMT>
+struct SplitRelu {
+  static constexpr bool value = FMT == FMT_MXFP4;
+};
+
 // Query-side operands of one row, held in registers for the life of a wave.
 template <int FMT, int H>
 struct RowOperand {
   static constexpr int MT = H / 32;
   v8i a[MT][2];
   int sa[MT];  // e8m0 block scales of the two K-steps, byte ks (the MFMA's scale byte select)
-  float w[MT][16];
+  float w[MT][16];  // w of this lane's heads (halved for the split form)
 };
 
 template <int FMT, int H>
@@ -90,10 +98,11 @@ __device__ __forceinline__ void load_row(RowOperand<FMT, H>& ro, const ScoreArgs
     } else {
       ro.sa[mt] = (int)A.q_sf[hv * 4 + half] | ((int)A.q_sf[hv * 4 + 2 + half] << 8);
     }
+    constexpr float kW = SplitRelu<FMT>::value ? 0.5f : 1.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int h = mt * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-      ro.w[mt][i] = bf16_to_f32(A.w[(int64_t)r * H + h]);
+      ro.w[mt][i] = kW * bf16_to_f32(A.w[(int64_t)r * H + h]);
     }
   }
 }
