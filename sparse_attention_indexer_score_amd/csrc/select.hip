@@ -40,6 +40,7 @@ __device__ __forceinline__ int64_t row_span(int64_t ld, const int32_t* row_start
   return (int64_t)r * ld + rs;
 }
 
+template <bool LONG>
 __global__ __launch_bounds__(kSelThreads, 8) void select_rows_kernel(const float* x, int64_t ld,
                                                                   const int32_t* row_start, const int32_t* len,
                                                                   int32_t k, int32_t* out) {
@@ -52,10 +53,11 @@ __global__ __launch_bounds__(kSelThreads, 8) void select_rows_kernel(const float
     for (int j = threadIdx.x; j < n; j += kSelThreads) o[j] = j;
   } else if (m > 0) {
     const float* xr = x + off;
+    constexpr int SAMP = LONG ? kSelSamplesLong : kSelSamples, SEG = LONG ? 8 : 64;
     if ((reinterpret_cast<uintptr_t>(xr) & 15) == 0 && n >= 4)  // workgroup-uniform
-      block_select_sampled<kSelThreads, true>(xr, n, m, o, sm);
+      block_select_sampled<kSelThreads, true, SelSmemT<kSelCand>, SAMP, SEG>(xr, n, m, o, sm);
     else
-      block_select_sampled<kSelThreads, false>(xr, n, m, o, sm);
+      block_select_sampled<kSelThreads, false, SelSmemT<kSelCand>, SAMP, SEG>(xr, n, m, o, sm);
   }
   for (int j = m + threadIdx.x; j < k; j += kSelThreads) o[j] = -1;
 }
@@ -243,7 +245,11 @@ __global__ __launch_bounds__(kSelThreads) void mb_refine_kernel(const float* x, 
 hipError_t launch_select_single(const float* x, int64_t ld, const int32_t* row_start, const int32_t* len,
                                 int32_t rows, int32_t k, int32_t* out, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  select_rows_kernel<<<dim3(rows), dim3(kSelThreads), 0, s>>>(x, ld, row_start, len, k, out);
+  // Rows of a pitch of 2^18 or more take the long-row sample (6144 keys in runs of 8).
+  if (ld >= (int64_t)1 << 18)
+    select_rows_kernel<true><<<dim3(rows), dim3(kSelThreads), 0, s>>>(x, ld, row_start, len, k, out);
+  else
+    select_rows_kernel<false><<<dim3(rows), dim3(kSelThreads), 0, s>>>(x, ld, row_start, len, k, out);
   return hipGetLastError();
 }
 

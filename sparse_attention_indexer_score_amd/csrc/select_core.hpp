@@ -433,8 +433,8 @@ __device__ uint32_t block_kth_key(const Src& src, int n, int m, SM& sm, bool zer
 }
 
 // Top-m of a materialised row x[0..n) (1 <= m < n) with one full pass over it:
-//   1. rows longer than the candidate buffer take a sample of kSelSamples order keys in
-//      NSEG evenly spaced runs of consecutive elements (a few per cent of the row) and a
+//   1. rows longer than the candidate buffer take a sample of SAMP order keys in
+//      SAMP / SEG evenly spaced runs of SEG consecutive elements and a
 //      threshold T = the lower edge of the 12-bit bin of the sample's r-th largest key
 //      (keys normalised over the sample's range), r = ceil(1.75 m samples / n), so that
 //      about 1.75 m elements of the row are expected at or above T, well inside [m, kCap]
@@ -446,13 +446,19 @@ __device__ uint32_t block_kth_key(const Src& src, int n, int m, SM& sm, bool zer
 //      [T, max] and the radix levels 1.. refine it in LDS; otherwise block_select() reruns
 //      the row exactly with full passes.
 // The result is exact either way; the sample only decides how much work is done.
+// Sample shapes: 2048 keys in 32 runs of 64 (one or two cache lines each) for rows of up to
+// a few hundred thousand elements; 6144 keys in 768 runs of 8 for longer rows, where r would
+// otherwise fall to single digits and a few runs landing on (or missing) clustered high
+// values move T far enough that the count leaves [m, kCap].
 constexpr int kSelSamples = 2048;
+constexpr int kSelSamplesLong = 6144;
 
 // VEC: x is 16-byte aligned and n >= 4 (the 16-byte path; otherwise the 4-byte path only).
-template <int NT, bool VEC, class SM>
+template <int NT, bool VEC, class SM, int SAMP = kSelSamples, int SEG = 64>
 __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out, SM& sm) {
-  static_assert(SM::kCap >= kSelSamples, "the sample lives in the candidate buffer");
-  constexpr int SEG = 64, NSEG = kSelSamples / SEG;  // 32 runs of 64 consecutive keys
+  static_assert(SM::kCap >= SAMP, "the sample lives in the candidate buffer");
+  static_assert(SAMP % SEG == 0 && SAMP / SEG >= 2, "whole runs");
+  constexpr int NSEG = SAMP / SEG;
   const int l = lane_id();
   // Streaming pass state: 16-byte loads, UV per thread per step, the next step's loads
   // issued before this step's keys are tested.  The first step's loads do not depend on
@@ -474,8 +480,8 @@ __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out,
   };
   // The sample's loads go first: loads complete in order, so the sample can be ranked while
   // the first step is still in flight (the barriers up to the streaming pass order LDS only).
-  constexpr int SPT = kSelSamples / NT;
-  static_assert(kSelSamples % NT == 0, "whole sample elements per thread");
+  constexpr int SPT = SAMP / NT;
+  static_assert(SAMP % NT == 0, "whole sample elements per thread");
   float sv[SPT];
   if (n > SM::kCap) {
 #pragma unroll
@@ -511,9 +517,9 @@ __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out,
     zero_hist<NT>(sm, kHistBins);  // the sample's radix level, cleared under the same barrier
     lds_sync();
     const KeyNorm nz = key_norm(sm.kmin, sm.kmax);
-    int64_t rank = ((int64_t)7 * m * kSelSamples + (int64_t)4 * n - 1) / ((int64_t)4 * n);  // ceil(1.75 m S / n)
-    rank = rank < 1 ? 1 : (rank > kSelSamples ? kSelSamples : rank);
-    T = nz.denormalize(block_kth_key<NT, NormLdsKeySrc, SM, 1>(NormLdsKeySrc{sm.tkey, nz}, kSelSamples, (int)rank,
+    int64_t rank = ((int64_t)7 * m * SAMP + (int64_t)4 * n - 1) / ((int64_t)4 * n);  // ceil(1.75 m S / n)
+    rank = rank < 1 ? 1 : (rank > SAMP ? SAMP : rank);
+    T = nz.denormalize(block_kth_key<NT, NormLdsKeySrc, SM, 1>(NormLdsKeySrc{sm.tkey, nz}, SAMP, (int)rank,
                                                                  sm, true));
     lds_sync();
   }

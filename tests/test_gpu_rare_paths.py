@@ -193,3 +193,26 @@ def test_fused_66000_rows():
     sch = sc.cpu().numpy()
     for r in sample[::10]:
         assert np.array_equal(sch[r, :p.ke[r]], oracle.row_scores(p, r)), r
+
+
+@pytest.mark.parametrize("k", [512, 2048])
+def test_select_long_rows(k):
+    """Rows of pitch >= 2^18 (the long-row sample: 6144 keys in runs of 8): lengths from
+    below the candidate buffer to the whole pitch, with clustered runs of high values (as
+    the long workload plants them) and ties; every row equals the oracle's selection, with
+    the sampled route and with one workgroup per row forced."""
+    rng = np.random.default_rng(90 + k)
+    rows, ld = 20, 300000
+    x = rng.standard_normal((rows, ld)).astype(np.float32)
+    for r in range(rows):                     # runs of 16..64 high values, about 2k in all
+        for _ in range(rng.integers(20, 60)):
+            at, ln = int(rng.integers(0, ld - 64)), int(rng.integers(16, 65))
+            x[r, at:at + ln] = (3.0 + 0.5 * rng.standard_normal(ln)).astype(np.float32)
+    x[:, ::97] = np.float32(2.5)              # ties
+    n = np.array([ld, ld - 1, 1000, 6144, 6145, 2 * k, k, k - 1, 0, 262144] +
+                 list(rng.integers(0, ld + 1, size=rows - 10)), dtype=np.int32)
+    ref = oracle.select_rows(x, n, k)
+    xd, nd = torch.from_numpy(x).cuda(), torch.from_numpy(n).cuda()
+    for split in (None, 0):
+        got = sai.idx_select(xd, nd, k, split=split).cpu().numpy()
+        same_sets(got, ref, f"long rows, k={k}, split={split}")
