@@ -102,15 +102,19 @@ struct TileWork {
 //  - At least 8 chunks and spread (paged keys: a row block's keys are its own, so an XCD
 //    gains nothing from holding whole chunks): item (c, j) runs on XCD (c + j) % 8.  Later
 //    chunks hold less work (fewer rows reach them), and this keeps the XCDs' shares even.
-//    Same grid.
+//    The chunk groups are dealt last first.  Same grid.
 //  - Fewer chunks: XCD x takes the x-th eighth of the items, so every XCD has work.  Grid:
 //    8 * ceil(total / 8) workgroups.
 __device__ __forceinline__ int64_t map_item(const TileWork& W) {
   const int64_t b = blockIdx.x;
   const int64_t x = b & 7, local = b >> 3;
   if (W.nchunk < 8) return x * ((W.total + 7) / 8) + local;
-  const int64_t g = local / W.nrb, j = local % W.nrb;
+  int64_t g = local / W.nrb;
+  const int64_t j = local % W.nrb;
   if (!W.spread) return (g * 8 + x) * W.nrb + j;
+  // Paged keys: chunk groups in reverse, so that the last chunks of the longest requests (few
+  // items among many empty ones) start first and the dense first chunks fill the end.
+  g = (W.nchunk + 7) / 8 - 1 - g;
   // Chunk c of group g gives XCD x its row blocks r0, r0 + 8, ... with r0 = (x - c) mod 8;
   // over the group's 8 chunks those are nrb items, taken chunk by chunk.
   int64_t rem = j;
@@ -662,8 +666,8 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
 #pragma unroll
     for (int r = 0; r < RW; ++r) mfma_row<FMT, H>(a.row[r], ro[r], ko);
   };
-  // Head reduce of all RW rows; at 4 rows per wave the rows' chains are interleaved for
-  // instruction-level parallelism.  Each row's own sum runs over its heads in one fixed order.
+  // Head reduce of all RW rows, the rows' chains interleaved for instruction-level
+  // parallelism.  Each row's own sum runs over its heads in one fixed order.
   // term(x): |x| (split form) or max(x, 0) (direct form).
   auto term = [](float x) -> float {
     if constexpr (kSplit) return __builtin_fabsf(x);
@@ -673,23 +677,13 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
     float part[RW];
 #pragma unroll
     for (int r = 0; r < RW; ++r) part[r] = 0.0f;
-    if constexpr (RW >= 4) {
 #pragma unroll
-      for (int mt = 0; mt < H / 32; ++mt)
+    for (int mt = 0; mt < H / 32; ++mt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
+      for (int i = 0; i < 16; ++i)
 #pragma unroll
-          for (int r = 0; r < RW; ++r)
-            part[r] = __builtin_fmaf(ro[r].w[mt][i], term(a.row[r][mt][i]), part[r]);
-    } else {  // same sums, row after row (fewer live registers)
-#pragma unroll
-      for (int r = 0; r < RW; ++r)
-#pragma unroll
-        for (int mt = 0; mt < H / 32; ++mt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            part[r] = __builtin_fmaf(ro[r].w[mt][i], term(a.row[r][mt][i]), part[r]);
-    }
+        for (int r = 0; r < RW; ++r)
+          part[r] = __builtin_fmaf(ro[r].w[mt][i], term(a.row[r][mt][i]), part[r]);
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const float hs = combine_halves(part[2 * p], part[2 * p + 1]);
