@@ -796,23 +796,30 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
     const int tbase = tA + st * G::kTiles;
     const StageBase sbase = stage_base(buf);
     bool whole = false;  // wave-uniform: every tile of the stage is this wave's and inside all its rows
-    if constexpr (!SHARED && RW >= 4)  // (a second copy of the tile loop; 2-row kernels lack the registers)
-      whole = tbase >= wt0 && tbase + G::kTiles <= min(wt1, tB) && tbase * kTile >= full_lo &&
-              (tbase + G::kTiles) * kTile <= full_hi;
+    // A second copy of the tile loop: 4-row kernels, and the 2-row FILTER kernels (the
+    // 2-row STORE and SAMPLE kernels would spill).  Shared rows (paged keys) with two waves
+    // per row pair: each wave's tiles i = slot, slot + 2, ... of the stage.
+    constexpr bool kWhole = RW >= 4 || MODE == MODE_FILTER;
+    constexpr int kStep = SHARED ? 2 : 1;
+    if constexpr (kWhole)
+      whole = (SHARED ? split == 2 && slot >= 0 : (tbase >= wt0 && tbase + G::kTiles <= min(wt1, tB))) &&
+              tbase + G::kTiles <= tB && tbase * kTile >= full_lo && (tbase + G::kTiles) * kTile <= full_hi;
     if (whole) {
-      if constexpr (!SHARED && RW >= 4) {
+      if constexpr (kWhole) {
         // The next tile's key operand is read from LDS once this tile's MFMAs are issued
         // (into the registers they have just read), so the LDS latency runs under this
         // tile's head reduce instead of stalling the next tile's MFMAs.
+        const int i0 = SHARED ? slot : 0;
         KeyOperand ko;
         float ksc;
-        read_b(sbase, 0, ko, ksc);
+        read_b(sbase, i0, ko, ksc);
 #pragma unroll
-        for (int i = 0; i < G::kTiles; ++i) {
+        for (int j = 0; j < G::kTiles / kStep; ++j) {
+          const int i = i0 + kStep * j;
           Acc a;
           issue(a, ko);
           const float ksc_i = ksc;
-          if (i + 1 < G::kTiles) read_b(sbase, i + 1, ko, ksc);
+          if (j + 1 < G::kTiles / kStep) read_b(sbase, i + kStep, ko, ksc);
           float sc[NP];
           reduce(a, ksc_i, sc);
           epilogue(tbase + i, sc, true);
