@@ -112,6 +112,27 @@ def step_ms(fn, iters, flush=None):
     return sorted(a.elapsed_time(b) for a, b in marks)
 
 
+def graph_ms(fn, iters, flush=None):
+    """Sorted per-replay HIP-event times (ms) of one call of fn() captured into a HIP graph
+    (launch gaps between the call's kernels removed); flush() runs eagerly before every
+    replay, outside its events.  The replays' results are those of an eager call (the library
+    records kernel launches only)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fn()
+    torch.cuda.synchronize()
+    ms = step_ms(g.replay, iters, flush)
+    del g
+    return ms
+
+
 def timed_ms(fn, iters, flush=None):
     """Median and minimum of step_ms."""
     ms = step_ms(fn, iters, flush)
@@ -144,6 +165,7 @@ def fused_leg(p, dev, iters, flush, what):
     runner()
     torch.cuda.synchronize()
     ms = step_ms(runner, iters, flush)
+    gms = graph_ms(runner, iters, flush)
     stages = stage_pass(runner, iters, flush)
     med = ms[len(ms) // 2]
     alg = p.pairs * 2 * 128 * p.heads
@@ -153,7 +175,8 @@ def fused_leg(p, dev, iters, flush, what):
            "score_filter_ms": round(k2, 4), "score_filter_TFLOPs": round(alg / (k2 * 1e-3) / 1e12, 1),
            "score_filter_frac": round(alg / (k2 * 1e-3) / 1e12 / PEAK_TFLOPS[p.fmt], 4),
            "peak_TFLOPs": PEAK_TFLOPS[p.fmt], "stage_ms": {s: round(v, 4) for s, v in stages.items()},
-           "fallback_rows": st["fallback_rows"]}
+           "fallback_rows": st["fallback_rows"],
+           "graph_ms": round(gms[len(gms) // 2], 4), "graph_min_ms": round(gms[0], 4)}
     del runner, dp
     torch.cuda.empty_cache()
     return res
@@ -402,6 +425,9 @@ def main():
     log(f"[bench] {args.steps} steps: median {ms:.3f} ms, min {ms_steps[0]:.3f} ms, mean "
         f"{float(np.mean(ms_steps)):.3f} ms (wall {wall * 1e3 / args.steps:.3f} ms/step incl. flushes)")
     warm_ms = float(np.mean(step_ms(runner, args.steps)))
+    # The same call captured into a HIP graph and replayed (flushed the same way).
+    g_steps = graph_ms(runner, args.steps, flush)
+    log(f"[bench] graph replays: median {g_steps[len(g_steps) // 2]:.3f} ms, min {g_steps[0]:.3f} ms")
     # Stage split from a separate pass of the same flushed steps (the library's own events on
     # its launch stream), so that the timed steps record nothing but their own two events.
     stage_ms = stage_pass(runner, args.steps, flush)
@@ -443,7 +469,9 @@ def main():
         "fused_topk_ms": round(ms, 4),
         "fused_topk_min_ms": round(ms_steps[0], 4),
         "fused_topk_warm_ms": round(warm_ms, 4),
-        "timing": "median of the timed steps, each cold (L2 and MALL flushed by a 512 MiB fill before it)",
+        "fused_topk_graph_ms": round(g_steps[len(g_steps) // 2], 4),
+        "timing": "median of the timed steps, each cold (L2 and MALL flushed by a 512 MiB fill before it); "
+                  "fused_topk_graph_ms: the same call captured into a HIP graph and replayed, flushed the same way",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
