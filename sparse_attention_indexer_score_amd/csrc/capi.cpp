@@ -16,7 +16,6 @@ using namespace idx;
 namespace {
 
 constexpr int32_t kVersion = 1 * 10000 + 0 * 100 + 0;
-constexpr int kFallbackBlocks = 32;  // workgroups that serve the exact fallback queue
 constexpr size_t kAlign = 256;
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -109,7 +108,7 @@ FusedSizes fused_sizes(const idx_problem* p, int32_t k) {
   z.stride = sample_stride_for(k);
   z.ns = (int32_t)((z.key_span + z.stride - 1) / z.stride);
   if (z.ns < 1) z.ns = 1;
-  z.fb_blocks = std::max(1, std::min(p->rows, kFallbackBlocks));
+  z.fb_blocks = std::max(1, std::min(p->rows, kFbSlots));
   z.scratch_ld = (int64_t)round_up((size_t)std::max<int64_t>(z.key_span, 1), 64);
   const size_t rows = (size_t)std::max(p->rows, 1);
   size_t o = 0;
@@ -120,7 +119,7 @@ FusedSizes fused_sizes(const idx_problem* p, int32_t k) {
   z.off_stats = o;
   o = round_up(o + kStatSlots * 8, kAlign);
   z.off_fb = o;
-  o = round_up(o + 8 + rows * 4, kAlign);
+  o = round_up(o + kFbCtrlWords * 4 + rows * 4, kAlign);
   z.off_slab_s = o;
   o = round_up(o + rows * (size_t)z.cap * 4, kAlign);
   z.off_slab_i = o;
@@ -306,10 +305,12 @@ int idx_fused_topk(const idx_problem* p, int32_t k, int32_t* out_idx, void* ws, 
   if (p->rows == 0) return IDX_OK;
   if (!ws || ws_bytes < z.total) return IDX_EWS;
   if (!aligned(ws, kAlign)) return IDX_EALIGN;
-  if ((rc = current_device(nullptr))) return rc;
+  int cu = 0;
+  if ((rc = current_device(&cu))) return rc;
   char* base = static_cast<char*>(ws);
   FusedPlan F;
   F.k = k;
+  F.cu = cu;
   F.cap = z.cap;
   F.stride = z.stride;
   F.ns = z.ns;
@@ -323,7 +324,7 @@ int idx_fused_topk(const idx_problem* p, int32_t k, int32_t* out_idx, void* ws, 
   F.stats = reinterpret_cast<long long*>(base + z.off_stats);
   F.want_stats = stats != nullptr;
   F.fb_ctrl = reinterpret_cast<int32_t*>(base + z.off_fb);
-  F.fb_list = F.fb_ctrl + 2;
+  F.fb_list = F.fb_ctrl + kFbCtrlWords;
   F.slab_s = reinterpret_cast<float*>(base + z.off_slab_s);
   F.slab_i = reinterpret_cast<int32_t*>(base + z.off_slab_i);
   F.samp = reinterpret_cast<float*>(base + z.off_samp);

@@ -451,8 +451,9 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
       } else {
         plo[i] = ks;
         phi[i] = ke;
-        // stored scores stay inside the caller's row pitch whatever the device-side range
-        if (MODE == MODE_STORE && (int64_t)ke - ks > E.ld) phi[i] = ks + (int)E.ld;
+        // stored scores stay inside the row pitch (the caller's, or the fallback's scratch
+        // row) whatever the device-side range
+        if ((MODE == MODE_STORE || MODE == MODE_ROWSTORE) && (int64_t)ke - ks > E.ld) phi[i] = ks + (int)E.ld;
       }
     }
     if (phi[i] > plo[i]) {
@@ -999,7 +1000,7 @@ __global__ __launch_bounds__(kThrThreads) void threshold_kernel(ThrArgs T) {
   uint32_t kv[PER];  // this thread's sample keys j = thread + kThrThreads e (staged rows)
   const int r = blockIdx.x;
   if (r == 0 && threadIdx.x < kStatSlots) T.stats[threadIdx.x] = (threadIdx.x == kStatMin) ? 0x7FFFFFFF : 0;
-  if (r == 0 && threadIdx.x < 2) T.fb_ctrl[threadIdx.x] = 0;
+  if (r == 0 && threadIdx.x < kFbCtrlWords) T.fb_ctrl[threadIdx.x] = 0;
   const int ks = T.ks[r], ke = T.ke[r];
   const int V = ke - ks;
   if (threadIdx.x == 0) T.cnt[r] = 0;
@@ -1203,47 +1204,141 @@ struct FbArgs {
   int64_t scratch_ld;
   int32_t* out;
   int32_t k, tie_cap;
+  int32_t nslots;       // scratch rows (<= kFbSlots)
+  int32_t row_tiles;    // tiles a row's keys can span
 };
 
+// Top-need of the V scores at x into out (row-relative key indices), exact: the sampled
+// select (one pass over the scores in most cases), with the sample idx_select takes for
+// long rows (6144 keys in runs of 8; rows of up to 6144 keys take every key) for any row
+// length, the better estimate on clustered scores; the full radix passes when the
+// tie-capacity override asks for them or for rows under 4 keys.  8 16-byte loads per
+// thread in flight in the streaming pass.  (One sample shape and this width keep the
+// fallback kernel within its registers: no private-memory spills.)
+template <int NT, class SM>
+__device__ __forceinline__ void fb_select_row(const float* x, int V, int need, int32_t* out, SM& sm, int tie_cap) {
+  const bool vec = (reinterpret_cast<uintptr_t>(x) & 15) == 0 && V >= 4;  // workgroup-uniform
+  if (need >= V || !vec || tie_cap < kTieCap) {
+    if (need > 0) block_select<NT>(RowSrc{x}, V, need, out, sm, tie_cap);
+  } else {
+    block_select_sampled<NT, true, SM, kSelSamplesLong, 8, 8>(x, V, need, out, sm);
+  }
+}
 
+// K4: exact fallback for the rows K3 queued, in one launch that exits at once when the
+// queue is empty.
+//  1. The first Q = min(queued, nslots) queued rows are re-scored over the whole grid: work
+//     item w is chunk w % nchunk of queue entry w / nchunk, scored into scratch row
+//     w / nchunk.  The chunk length (at least 128 tiles) is chosen from Q so that the
+//     grid's workgroups (about one per CU) take about one item each; chunks are whole
+//     tiles, so no key is written twice.
+//  2. After each item the workgroup releases its stores (device scope: each XCD's L2 is
+//     written back) and counts the item in the entry's counter; the workgroup that counts
+//     the entry's last chunk acquires (its L2 invalidated) and selects the row from its
+//     scratch row.
+//  3. That workgroup then owns the scratch row and takes further queue entries (a queue
+//     longer than nslots) from the shared head, scoring each whole row into it and
+//     selecting.
+// No workgroup waits on another.  The row is re-scored by wg_tiles() with the same per-key
+// arithmetic as the score kernels (contiguous or paged keys; here each wave takes two tiles
+// of every stage).  A row's score does not depend on which rows share its wave or which
+// workgroup scores which tiles: its MFMA outputs, its head reduce, the half-wave sum (low
+// half + high half) and its linear-tile pieces are computed the same way for any pairing,
+// so the scores are bitwise the ones the slab was filtered with.  Only the row itself is
+// stored; 2 rows per wave keep the register budget of this LDS-heavy kernel.  The stage
+// buffers and the select's LDS are never live at once and share one union.
+template <int FMT>
+union FbShared {
+  SelSmemT<kSelSamplesLong> sel;  // tie buffer, or the sampled select's sample and candidates
+  StageShared<FMT> stage;
+};
 
-// The row is re-scored by wg_tiles() with the same per-key arithmetic as the score kernels
-// (contiguous or paged keys; here each wave takes two tiles of every stage).  A row's score does
-// not depend on which rows share its wave: its MFMA outputs, its head reduce, the half-wave
-// sum (low half + high half) and its linear-tile pieces are computed the same way for any
-// pairing, so the scores are bitwise the ones the slab was filtered with.  Only the row
-// itself is stored; 2 rows per wave keep the register budget of this LDS-heavy kernel.
 template <int FMT, int H>
-__global__ __launch_bounds__(kThreads) void fallback_tiles_kernel(ScoreArgs A, LinArgs L, FbArgs F) {
+__global__ __launch_bounds__(kThreads) void fallback_kernel(ScoreArgs A, LinArgs L, FbArgs F) {
   constexpr int RW = 2;
-  __shared__ SelSmem sm;
-  __shared__ StageShared<FMT> sh;
-  __shared__ int sh_item;
-  float* mine = F.scratch + (int64_t)blockIdx.x * F.scratch_ld;
-  const StageLds<FMT> sl{sh.codes, sh.sf, sh.ks};
-  for (;;) {
-    if (threadIdx.x == 0) sh_item = atomicAdd(&F.fb_ctrl[1], 1);
-    __syncthreads();
-    const int item = sh_item;
-    __syncthreads();
-    if (item >= F.fb_ctrl[0]) break;  // every wave sees the same item and count
-    const int r = F.fb_list[item];
+  __shared__ FbShared<FMT> shu;
+  __shared__ int sh_word;
+  const StageLds<FMT> sl{shu.stage.codes, shu.stage.sf, shu.stage.ks};
+  const int queued = F.fb_ctrl[0];
+  int32_t* done = F.fb_ctrl + 2;
+  // Visible keys of row r, clamped to the scratch row (an invalid range counts as empty or
+  // stays inside scratch).
+  auto len_of = [&](int r) {
+    const int64_t v = (int64_t)A.ke[r] - A.ks[r];
+    return (int)(v < 0 ? 0 : (v > F.scratch_ld ? F.scratch_ld : v));
+  };
+  // Scores of tiles [t0, t1) of row r (clamped to its keys) into scratch row `slot`.
+  auto score_tiles = [&](int r, int slot, int t0, int t1) {
     const int ks = A.ks[r], ke = A.ke[r];
-    const int V = max(ke - ks, 0);
-    if (V > 0) {
-      EpiArgs E = {};
-      E.out = mine;
-      E.only_row = r;
-      const int req = A.page_table ? request_of(A, r) : -1;
-      wg_tiles<FMT, H, MODE_ROWSTORE, RW, true>(A, L, E, (r / RW) * RW, 0, 1, ks, ke, ks / kTile,
-                                                (ke + kTile - 1) / kTile, sl, req, 1u << (r % RW));
+    const int lo = ks > t0 * kTile ? ks : t0 * kTile, hi = ke < t1 * kTile ? ke : t1 * kTile;
+    EpiArgs E = {};
+    E.out = F.scratch + (int64_t)slot * F.scratch_ld;
+    E.ld = F.scratch_ld;
+    E.only_row = r;
+    const int req = A.page_table ? request_of(A, r) : -1;
+    wg_tiles<FMT, H, MODE_ROWSTORE, RW, true>(A, L, E, (r / RW) * RW, 0, 1, lo, hi, t0, t1, sl, req,
+                                              1u << (r % RW));
+  };
+  const int Q = queued < F.nslots ? queued : F.nslots;
+  constexpr int kMinChunk = 128;  // tiles (4096 keys)
+  const int64_t want = ((int64_t)Q * F.row_tiles + gridDim.x - 1) / gridDim.x;
+  const int chunk = (int)(want > kMinChunk ? want : kMinChunk);
+  const int nchunk = (F.row_tiles + chunk - 1) / chunk;
+  const int64_t items = (int64_t)Q * nchunk;
+  int64_t w = blockIdx.x;  // next chunk item of this workgroup
+  int own = -1;            // scratch row this workgroup owns after selecting its row
+  // One loop (one inlined copy of the score and select code): chunk items first, then,
+  // for a workgroup that owns a scratch row, whole rows from the shared head.
+  for (;;) {  // workgroup-uniform
+    int r, slot, t0, t1;
+    const bool chunked = w < items;
+    if (chunked) {
+      slot = (int)(w / nchunk);
+      const int c = (int)(w % nchunk);
+      r = F.fb_list[slot];
+      t0 = A.ks[r] / kTile + c * chunk;
+      const int tend = (A.ke[r] + kTile - 1) / kTile;
+      t1 = tend < t0 + chunk ? tend : t0 + chunk;
+    } else {
+      if (own < 0) break;
+      if (threadIdx.x == 0) sh_word = F.nslots + atomicAdd(&F.fb_ctrl[1], 1);
+      __syncthreads();
+      const int item = sh_word;
+      __syncthreads();
+      if (item >= queued) break;
+      r = F.fb_list[item];
+      slot = own;
+      t0 = A.ks[r] / kTile;
+      t1 = (A.ke[r] + kTile - 1) / kTile;
     }
-    __syncthreads();
-    const int need = min(F.k, V);
-    int32_t* out = F.out + (int64_t)r * F.k;
-    if (need > 0) block_select<kThreads>(RowSrc{mine}, V, need, out, sm, F.tie_cap);
-    for (int j = need + threadIdx.x; j < F.k; j += kThreads) out[j] = -1;
-    __syncthreads();
+    if (len_of(r) > 0 && t0 < t1) score_tiles(r, slot, t0, t1);
+    bool sel = !chunked;
+    if (chunked) {
+      // Every wave releases its own scores at device scope (L2 written back once its
+      // stores have completed: a workgroup barrier does not wait for other waves' global
+      // stores), then one increment, itself a release, counts the chunk.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __syncthreads();  // also: the stage buffers are reused next
+      if (threadIdx.x == 0)
+        sh_word = __hip_atomic_fetch_add(&done[slot], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      sel = sh_word == nchunk - 1;  // the entry's last chunk: its row is complete
+      __syncthreads();              // sh_word is rewritten next
+      if (sel) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        own = slot;
+      }
+      w += gridDim.x;
+    } else {
+      __syncthreads();
+    }
+    if (sel) {
+      const int V = len_of(r), need = min(F.k, V);
+      int32_t* out = F.out + (int64_t)r * F.k;
+      fb_select_row<kThreads>(F.scratch + (int64_t)slot * F.scratch_ld, V, need, out, shu.sel, F.tie_cap);
+      for (int j = need + threadIdx.x; j < F.k; j += kThreads) out[j] = -1;
+      __syncthreads();  // the LDS union is reused next
+    }
   }
 }
 
@@ -1459,7 +1554,9 @@ hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_id
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(4)) != hipSuccess) return e;
   }
-  // K4: exact fallback for queued rows (exits at once when the queue is empty)
+  // K4: exact fallback for queued rows (exits at once when the queue is empty): the first
+  // fb_blocks queued rows re-scored in chunks over the whole chip and selected, any further
+  // rows scored and selected one workgroup per row.
   {
     const ScoreArgs A = score_args(P);
     FbArgs B;
@@ -1470,13 +1567,16 @@ hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_id
     B.out = out_idx;
     B.k = F.k;
     B.tie_cap = F.tie_cap;
-    const dim3 grid(F.fb_blocks), block(kThreads);
+    B.nslots = F.fb_blocks;
+    B.row_tiles = (int)((F.scratch_ld + kTile - 1) / kTile + 1);  // key span + alignment
+    const int64_t items = (int64_t)B.nslots * ((B.row_tiles + 127) / 128);  // at the shortest chunks
+    const dim3 grid((unsigned)(items < F.cu ? items : F.cu)), block(kThreads);  // one workgroup per CU
     if (P.fmt == FMT_E4M3) {  // contiguous or paged
-      if (P.heads == 64) fallback_tiles_kernel<FMT_E4M3, 64><<<grid, block, 0, s>>>(A, L, B);
-      else fallback_tiles_kernel<FMT_E4M3, 32><<<grid, block, 0, s>>>(A, L, B);
+      if (P.heads == 64) fallback_kernel<FMT_E4M3, 64><<<grid, block, 0, s>>>(A, L, B);
+      else fallback_kernel<FMT_E4M3, 32><<<grid, block, 0, s>>>(A, L, B);
     } else {
-      if (P.heads == 64) fallback_tiles_kernel<FMT_MXFP4, 64><<<grid, block, 0, s>>>(A, L, B);
-      else fallback_tiles_kernel<FMT_MXFP4, 32><<<grid, block, 0, s>>>(A, L, B);
+      if (P.heads == 64) fallback_kernel<FMT_MXFP4, 64><<<grid, block, 0, s>>>(A, L, B);
+      else fallback_kernel<FMT_MXFP4, 32><<<grid, block, 0, s>>>(A, L, B);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = mark(5)) != hipSuccess) return e;

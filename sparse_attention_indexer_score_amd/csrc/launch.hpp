@@ -24,9 +24,16 @@ struct DevProblem {
   int64_t key_span;  // logical key space: num_keys (contiguous) or max_pages * 64 (paged)
 };
 
+// Exact fallback: scratch rows (queued rows re-scored at once) and the control words ahead
+// of the queued-row list: [0] queued count, [1] head of the rows past the scratch rows,
+// [2, 2 + kFbSlots) chunks scored so far of each scratch row's row.
+constexpr int kFbSlots = 32;
+constexpr int kFbCtrlWords = 2 + kFbSlots;
+
 // Per-call plan of the fused path (sizes and workspace carve-up).
 struct FusedPlan {
   int32_t k, cap, stride, ns, fb_blocks;
+  int32_t cu;  // compute units of the device
   int32_t debug_mode, debug_row_mod;
   int32_t tie_cap;  // tie-buffer capacity of the slab select and the fallback (<= kTieCap)
   int64_t scratch_ld;
@@ -35,7 +42,7 @@ struct FusedPlan {
   int32_t* cnt;
   long long* stats;  // kStatSlots
   int32_t want_stats;  // update the route counters (only when the caller asks for them)
-  int32_t* fb_ctrl;  // [0] count, [1] head
+  int32_t* fb_ctrl;  // kFbCtrlWords control words
   int32_t* fb_list;
   float* slab_s;
   int32_t* slab_i;

@@ -246,7 +246,7 @@ hipError_t launch_select_single(const float* x, int64_t ld, const int32_t* row_s
                                 int32_t rows, int32_t k, int32_t* out, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   // Rows of a pitch of 2^18 or more take the long-row sample (6144 keys in runs of 8).
-  if (ld >= (int64_t)1 << 18)
+  if (ld >= kSelLongRow)
     select_rows_kernel<true><<<dim3(rows), dim3(kSelThreads), 0, s>>>(x, ld, row_start, len, k, out);
   else
     select_rows_kernel<false><<<dim3(rows), dim3(kSelThreads), 0, s>>>(x, ld, row_start, len, k, out);

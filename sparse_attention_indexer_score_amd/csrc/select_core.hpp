@@ -452,9 +452,12 @@ __device__ uint32_t block_kth_key(const Src& src, int n, int m, SM& sm, bool zer
 // values move T far enough that the count leaves [m, kCap].
 constexpr int kSelSamples = 2048;
 constexpr int kSelSamplesLong = 6144;
+constexpr int kSelLongRow = 1 << 18;  // rows of at least this many elements take the long sample
 
 // VEC: x is 16-byte aligned and n >= 4 (the 16-byte path; otherwise the 4-byte path only).
-template <int NT, bool VEC, class SM, int SAMP = kSelSamples, int SEG = 64>
+// UV: 16-byte loads per thread and step of the streaming pass (a multiple of 4; a narrow
+// workgroup takes more, to keep as many bytes in flight).
+template <int NT, bool VEC, class SM, int SAMP = kSelSamples, int SEG = 64, int UV = 4>
 __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out, SM& sm) {
   static_assert(SM::kCap >= SAMP, "the sample lives in the candidate buffer");
   static_assert(SAMP % SEG == 0 && SAMP / SEG >= 2, "whole runs");
@@ -463,7 +466,7 @@ __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out,
   // Streaming pass state: 16-byte loads, UV per thread per step, the next step's loads
   // issued before this step's keys are tested.  The first step's loads do not depend on
   // the threshold, so they are issued before the sample is taken and arrive under it.
-  constexpr int UV = 4;
+  static_assert(UV % 4 == 0, "whole groups of 4 vectors");
   const float4* xv = reinterpret_cast<const float4*>(x);
   const int nv = VEC ? n / 4 : 0;  // >= 1 with VEC
   float4 cur[UV], nxt[UV];
@@ -559,26 +562,29 @@ __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out,
       }
     }
   };
-  // Vector part: one append (one LDS atomic per wave) for all 4 * UV keys of a step.
+  // Vector part: one append (one LDS atomic per wave) for each 16 keys (4 vectors) of a step.
   for (int base = 0; VEC && base < nv; base += UV * NT) {
     load(nxt, base + UV * NT);  // past the end on the last step: re-reads of the last vector
-    uint32_t k_[4 * UV];
-    bool ok[4 * UV];
-    int ix_[4 * UV];
 #pragma unroll
-    for (int u = 0; u < UV; ++u) {
-      const int jv = base + u * NT + (int)threadIdx.x;
-      k_[4 * u + 0] = order_key(cur[u].x);
-      k_[4 * u + 1] = order_key(cur[u].y);
-      k_[4 * u + 2] = order_key(cur[u].z);
-      k_[4 * u + 3] = order_key(cur[u].w);
+    for (int g = 0; g < UV; g += 4) {
+      uint32_t k_[16];
+      bool ok[16];
+      int ix_[16];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        ok[4 * u + c] = jv < nv;
-        ix_[4 * u + c] = 4 * jv + c;
+      for (int u = 0; u < 4; ++u) {
+        const int jv = base + (g + u) * NT + (int)threadIdx.x;
+        k_[4 * u + 0] = order_key(cur[g + u].x);
+        k_[4 * u + 1] = order_key(cur[g + u].y);
+        k_[4 * u + 2] = order_key(cur[g + u].z);
+        k_[4 * u + 3] = order_key(cur[g + u].w);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          ok[4 * u + c] = jv < nv;
+          ix_[4 * u + c] = 4 * jv + c;
+        }
       }
+      append(k_, ok, ix_, std::integral_constant<int, 16>{});
     }
-    append(k_, ok, ix_, std::integral_constant<int, 4 * UV>{});
 #pragma unroll
     for (int u = 0; u < UV; ++u) cur[u] = nxt[u];
   }

@@ -3,8 +3,11 @@
 * Exact fallback (K4) forced on every workload format: MXFP4 with 32 heads (four rows per
   wave in the score kernel, two in the fallback) and paged e4m3 keys, with the threshold
   forced to +inf (every sampled row underflows), to -inf (rows longer than the slab
-  overflow), on every third row, and with a small slab.  The result must equal the
-  oracle's selection over the GPU's materialised scores, bit for bit.
+  overflow), on every third row, and with a small slab; key spans within one fallback
+  chunk and across many (the queued rows then re-scored by many workgroups, the first
+  32 of them, and the rest row by row), and rows of 2^18 keys or more (the fallback's
+  sampled select with the long-row sample).  The result must equal the oracle's selection
+  over the GPU's materialised scores, bit for bit.
 * The slab select's tie-buffer overflow: more than 4096 equal candidates at the k-th
   value (every key a candidate: threshold -inf and a slab as long as the row), and the
   tie-capacity hook that sends ordinary rows through the rescan.
@@ -43,6 +46,12 @@ FAMILIES = {
     "long_mxfp4_32h": lambda: wl.long_context(rows=40, num_keys=12000, band_keys=2000, topk=256, seed=61),
     "decode_paged": lambda: wl.decode(num_req=6, ctx_lo=3000, ctx_hi=20000, topk=256, seed=62),
     "prefill_e4m3_64h": lambda: wl.prefill(rows=40, num_keys=5000, topk=256, seed=8),
+    # key spans of many 4K-key chunks: queued rows are re-scored by the parallel pass
+    # (the first 32 queued rows) and by the per-row pass (the rest)
+    "long_mxfp4_32h_wide": lambda: wl.long_context(rows=40, num_keys=40000, band_keys=3000, topk=256, seed=63),
+    "decode_paged_wide": lambda: wl.decode(num_req=10, ctx_lo=20000, ctx_hi=60000, topk=256, seed=64),
+    # rows of 2^18 keys or more: the fallback's select takes the long-row sample
+    "long_mxfp4_32h_300k": lambda: wl.long_context(rows=8, num_keys=300000, band_keys=3000, topk=256, seed=65),
 }
 
 
