@@ -171,7 +171,10 @@ size_t idx_score_workspace(const idx_problem* p);
  *   k        1 .. IDX_MAX_TOPK
  *   out_idx  int32 [rows][k]: the selected j (relative to row_start), -1 padded
  *   ws       workspace of idx_select_workspace(rows, ld, k) bytes (may be NULL when
- *            that is 0)
+ *            that is 0).  The row split keeps one counter per row in it and every call
+ *            leaves those at 0; on a workspace whose contents are not yet the library's
+ *            (say a fresh allocation) a split row may take the multi-pass route once, with
+ *            the same result.  Calls that share a workspace must not overlap.
  * NaN scores give undefined results.  Device-side row_start and len outside those bounds
  * are clamped into the row ([0, ld)), so reads stay inside scores[rows][ld] and writes
  * inside out_idx[rows][k].                                                            */

@@ -119,10 +119,11 @@ def _check(code: int, what: str):
 
 
 def _workspace(nbytes: int, device) -> torch.Tensor:
-    """uint8 device buffer whose data pointer is 256-byte aligned."""
+    """Zero-filled uint8 device buffer whose data pointer is 256-byte aligned (the selection's
+    row-split counters then start at the value every call leaves them at)."""
     if nbytes == 0:
         return torch.empty(0, dtype=torch.uint8, device=device)
-    buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    buf = torch.zeros(nbytes + 256, dtype=torch.uint8, device=device)
     off = (-buf.data_ptr()) % 256
     return buf[off:off + nbytes]
 

@@ -6,13 +6,14 @@
 //   split == 0  select_rows_kernel: one 1024-thread workgroup per row (a sampled threshold,
 //               one pass into an LDS candidate buffer, radix refinement in LDS; the
 //               multi-pass block_select when the sample misjudges the row)
-//   split >= 2  mb_hist_kernel    g workgroups per row add their segment's level-1
-//                                 histogram into a per-row global histogram
-//               mb_scatter_kernel every workgroup finds the boundary bin from it, writes
-//                                 its elements above the bin to the output and appends
-//                                 the bin's elements to a per-row tie buffer
-//               mb_refine_kernel  one workgroup per row refines the tie buffer in LDS,
-//                                 or reruns the whole row in rescan mode if it overflowed
+//   split >= 2  seg_collect_kernel g workgroups per row each take the row's sample and
+//                                  threshold T (the same in all of them), stream their
+//                                  segment of the row and append its candidates (order
+//                                  key >= T) to the row's buffer in the workspace
+//               seg_merge_kernel   one workgroup per row refines the row's candidates in
+//                                  LDS, or selects the whole row with the multi-pass
+//                                  block_select when a segment overflowed or the
+//                                  candidates are fewer than m
 #include "launch.hpp"
 #include "select_core.hpp"
 
@@ -62,182 +63,147 @@ __global__ __launch_bounds__(kSelThreads, 8) void select_rows_kernel(const float
   for (int j = m + threadIdx.x; j < k; j += kSelThreads) o[j] = -1;
 }
 
-struct SplitWs {
-  uint32_t* hist;  // [rows][4096]
-  int32_t* pos;    // [rows] output cursor
-  int32_t* tcnt;   // [rows] tie count
-  uint32_t* tkey;  // [rows][kTieCap]
-  int32_t* tidx;   // [rows][kTieCap]
+// Row split workspace, per row r: a buffer of kSelCand candidates (order key, row index),
+// the position counter its segments reserve space with (left at 0 by every call), the
+// row's threshold T, and one slot per segment (candidates written, largest key, whether
+// all of them were written).  Every row with m < n is split, whatever its length: a row no
+// longer than the candidate buffer is not sampled (T = 0) and all of its elements are
+// candidates.
+constexpr int kSplitMax = 32;
+
+struct SegWs {
+  uint32_t* ckey;   // [rows][kSelCand]
+  int32_t* cidx;    // [rows][kSelCand]
+  int32_t* ctr;     // [rows]
+  uint32_t* thr;    // [rows]
+  int32_t* slot;    // [rows][kSplitMax][3]
 };
 
-static SplitWs carve(void* ws, int rows) {
-  SplitWs W;
+static SegWs carve(void* ws, int rows) {
+  SegWs W;
   char* p = static_cast<char*>(ws);
-  W.hist = reinterpret_cast<uint32_t*>(p);
-  p += (size_t)rows * kHistBins * 4;
-  W.pos = reinterpret_cast<int32_t*>(p);
-  p += (size_t)rows * 4;
-  W.tcnt = reinterpret_cast<int32_t*>(p);
-  p += (size_t)rows * 4;
-  p = reinterpret_cast<char*>(((uintptr_t)p + 255) & ~(uintptr_t)255);
-  W.tkey = reinterpret_cast<uint32_t*>(p);
-  p += (size_t)rows * kTieCap * 4;
-  W.tidx = reinterpret_cast<int32_t*>(p);
+  auto take = [&](size_t bytes) {
+    char* q = p;
+    p += (bytes + 255) & ~(size_t)255;
+    return q;
+  };
+  W.ckey = reinterpret_cast<uint32_t*>(take((size_t)rows * kSelCand * 4));
+  W.cidx = reinterpret_cast<int32_t*>(take((size_t)rows * kSelCand * 4));
+  W.ctr = reinterpret_cast<int32_t*>(take((size_t)rows * 4));
+  W.thr = reinterpret_cast<uint32_t*>(take((size_t)rows * 4));
+  W.slot = reinterpret_cast<int32_t*>(take((size_t)rows * kSplitMax * 3 * 4));
   return W;
 }
 
 size_t select_split_ws_bytes(int32_t rows) {
-  size_t b = (size_t)rows * kHistBins * 4 + (size_t)rows * 8;
-  b = (b + 255) & ~(size_t)255;
-  b += (size_t)rows * kTieCap * 8;
-  return b + 256;
+  auto r256 = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  return 2 * r256((size_t)rows * kSelCand * 4) + 2 * r256((size_t)rows * 4) + r256((size_t)rows * kSplitMax * 12);
 }
 
-// Clears hist, pos and tcnt (contiguous at the start of the workspace).
-__global__ void zero_words_kernel(uint32_t* p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = 0;
-}
-
+// Segment `part` of g of a row of n elements: a multiple of 4 elements long, so that the
+// segments of a 16-byte aligned row start 16-byte aligned.
 __device__ __forceinline__ void segment(int n, int g, int part, int& lo, int& hi) {
-  const int seg = (n + g - 1) / g;
-  lo = min(n, part * seg);
+  const int seg = ((n + g - 1) / g + 3) & ~3;
+  lo = (int)min((int64_t)n, (int64_t)part * seg);
   hi = min(n, lo + seg);
 }
 
-__global__ __launch_bounds__(kSelThreads) void mb_hist_kernel(const float* x, int64_t ld, const int32_t* row_start,
-                                                              const int32_t* len, int32_t k, int32_t g, SplitWs W) {
-  __shared__ SelSmem sm;
-  const int r = blockIdx.x / g, part = blockIdx.x % g;
-  int n, m;
-  const int64_t row_off = row_span(ld, row_start, len, r, k, n, m);
-  if (m >= n) return;  // the refine kernel writes trivial rows
-  int lo, hi;
-  segment(n, g, part, lo, hi);
-  zero_hist<kSelThreads>(sm, kHistBins);
-  __syncthreads();
-  hist_level1<kSelThreads>(RowSrc{x + row_off + lo}, hi - lo, sm);
-  __syncthreads();
-  uint32_t* gh = W.hist + (int64_t)r * kHistBins;
-  for (int b = threadIdx.x; b < kHistBins; b += kSelThreads)
-    if (sm.hist[b]) atomicAdd(&gh[b], sm.hist[b]);
-}
-
-__device__ __forceinline__ void load_row_hist(SelSmem& sm, const uint32_t* gh) {
-  for (int b = threadIdx.x; b < kHistBins; b += kSelThreads) sm.hist[b] = gh[b];
-  __syncthreads();
-}
-
-// Elements above the boundary bin, and the bin's elements when they are kept for
-// refinement, are gathered in LDS first; one global atomic per workgroup and list then
-// reserves their places in the row's output and tie buffer.  At most m <= 2048 elements of
-// a row are above the bin (or in it, when it is selected whole) and at most kTieCap are in
-// it when ties are kept, so both lists fit.
-
-__global__ __launch_bounds__(kSelThreads) void mb_scatter_kernel(const float* x, int64_t ld,
-                                                                 const int32_t* row_start, const int32_t* len,
-                                                                 int32_t k, int32_t g, int32_t* out, SplitWs W) {
-  __shared__ SelSmem sm;
-  __shared__ int32_t eidx[kMaxTopK];
+__global__ __launch_bounds__(kSelThreads, 8) void seg_collect_kernel(const float* x, int64_t ld,
+                                                                    const int32_t* row_start, const int32_t* len,
+                                                                    int32_t k, int32_t g, SegWs W) {
+  using SM = SelSmemT<kSelCand>;
+  __shared__ SM sm;
+  __shared__ int sh_pos;
   const int r = blockIdx.x / g, part = blockIdx.x % g;
   int n, m;
   const int64_t off = row_span(ld, row_start, len, r, k, n, m);
-  if (m >= n) return;
-  load_row_hist(sm, W.hist + (int64_t)r * kHistBins);
-  find_boundary<kSelThreads>(sm, kHistBins, (uint32_t)m);
-  const uint32_t b1 = (uint32_t)sm.bnd_bin;
-  const uint32_t cnt = sm.bnd_count;
-  const bool all_bin = cnt == (uint32_t)m - sm.bnd_above;
-  const bool keep_ties = !all_bin && cnt <= (uint32_t)kTieCap;
-  if (threadIdx.x == 0) {
-    sm.nout = 0;
-    sm.ntie = 0;
-  }
-  __syncthreads();
+  if (m >= n) return;  // the merge kernel writes such rows whole
   int lo, hi;
   segment(n, g, part, lo, hi);
-  const int l = lane_id();
-  // U elements per thread and step, loaded unconditionally at clamped positions (a load under
-  // a branch is waited for before the next is issued); lanes past the end are masked.
-  constexpr int U = 4;
-  for (int base = lo; base < hi; base += U * kSelThreads) {
-    uint32_t key_[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = base + u * kSelThreads + (int)threadIdx.x;
-      key_[u] = order_key(x[off + (j < hi ? j : hi - 1)]);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = base + u * kSelThreads + (int)threadIdx.x;
-      const uint32_t key = key_[u], d = key >> (32 - kHistBits);
-      const uint64_t me = wave_ballot(j < hi && (d > b1 || (all_bin && d == b1)));
-      const uint64_t mt = wave_ballot(j < hi && keep_ties && d == b1);
-      int be = 0, bt = 0;
-      if (l == 0) {
-        if (me) be = atomicAdd(&sm.nout, __builtin_popcountll(me));
-        if (mt) bt = atomicAdd(&sm.ntie, __builtin_popcountll(mt));
-      }
-      be = readlane(be, 0);
-      bt = readlane(bt, 0);
-      if ((me >> l) & 1) eidx[be + mask_prefix(me)] = j;
-      if ((mt >> l) & 1) {
-        const int t = bt + mask_prefix(mt);
-        sm.tkey[t] = key;
-        sm.tidx[t] = j;
-      }
+  const float* xr = x + off;
+  // The sample of long rows (6144 keys in runs of 8) for every row length: a run-structured
+  // top band moves a sample of 32 runs of 64 too far from row to row, and each segment here
+  // streams only its own part of the row, so the sample's scattered lines cost the row one
+  // read (shared through L2 by its segments) rather than lines its own pass reads anyway.
+  constexpr int SAMP = kSelSamplesLong, SEG = 8;
+  uint32_t T;
+  if ((reinterpret_cast<uintptr_t>(xr + lo) & 15) == 0 && hi - lo >= 4)  // workgroup-uniform
+    T = sampled_collect<kSelThreads, true, SM, SAMP, SEG, 4>(xr, n, m, lo, hi - lo, sm);
+  else
+    T = sampled_collect<kSelThreads, false, SM, SAMP, SEG, 4>(xr, n, m, lo, hi - lo, sm);
+  const int c = sm.ntie;
+  const int cs = min(c, SM::kCap);
+  if (threadIdx.x == 0) sh_pos = cs > 0 ? atomicAdd(&W.ctr[r], cs) : 0;
+  __syncthreads();
+  const int pos = sh_pos;
+  // (the counter may hold anything on a workspace's first use: a place outside the buffer
+  // only sends the row to the exact path)
+  const bool ok = c <= SM::kCap && pos >= 0 && (int64_t)pos + cs <= SM::kCap;
+  if (ok) {
+    uint32_t* ck = W.ckey + (int64_t)r * kSelCand + pos;
+    int32_t* ci = W.cidx + (int64_t)r * kSelCand + pos;
+    for (int t = threadIdx.x; t < cs; t += kSelThreads) {
+      ck[t] = sm.tkey[t];
+      ci[t] = sm.tidx[t];
     }
   }
-  __syncthreads();
-  const int ne = sm.nout, nt = sm.ntie;
   if (threadIdx.x == 0) {
-    sm.bnd_bin = ne ? atomicAdd(&W.pos[r], ne) : 0;
-    sm.bnd_above = nt ? (uint32_t)atomicAdd(&W.tcnt[r], nt) : 0u;
-  }
-  __syncthreads();
-  const int ob = sm.bnd_bin, tb = (int)sm.bnd_above;
-  int32_t* o = out + (int64_t)r * k;
-  for (int t = threadIdx.x; t < ne; t += kSelThreads) o[ob + t] = eidx[t];
-  for (int t = threadIdx.x; t < nt; t += kSelThreads) {
-    W.tkey[(int64_t)r * kTieCap + tb + t] = sm.tkey[t];
-    W.tidx[(int64_t)r * kTieCap + tb + t] = sm.tidx[t];
+    int32_t* sl = W.slot + ((int64_t)r * kSplitMax + part) * 3;
+    sl[0] = cs;
+    sl[1] = (int32_t)sm.kmax;
+    sl[2] = ok ? 1 : 0;
+    if (part == 0) W.thr[r] = T;
   }
 }
 
-__global__ __launch_bounds__(kSelThreads) void mb_refine_kernel(const float* x, int64_t ld,
-                                                                const int32_t* row_start, const int32_t* len,
-                                                                int32_t k, int32_t* out, SplitWs W) {
-  __shared__ SelSmem sm;
+__global__ __launch_bounds__(kSelThreads) void seg_merge_kernel(const float* x, int64_t ld,
+                                                                  const int32_t* row_start, const int32_t* len,
+                                                                  int32_t k, int32_t g, int32_t* out, SegWs W) {
+  using SM = SelSmemT<kSelCand>;
+  __shared__ SM sm;
+  __shared__ int sh_total, sh_ok;
+  __shared__ uint32_t sh_kmax;
   const int r = blockIdx.x;
   int n, m;
   const int64_t off = row_span(ld, row_start, len, r, k, n, m);
   int32_t* o = out + (int64_t)r * k;
+  const float* xr = x + off;
   if (m >= n) {
     for (int j = threadIdx.x; j < n; j += kSelThreads) o[j] = j;
   } else {
-    load_row_hist(sm, W.hist + (int64_t)r * kHistBins);
-    find_boundary<kSelThreads>(sm, kHistBins, (uint32_t)m);
-    const uint32_t above = sm.bnd_above;
-    const uint32_t cnt = sm.bnd_count;
-    const uint32_t need = (uint32_t)m - above;
-    __syncthreads();
-    if (cnt == need) {
-      // every element of the boundary bin was emitted by the scatter kernel
-    } else if (cnt <= (uint32_t)kTieCap) {
-      for (int t = threadIdx.x; t < (int)cnt; t += kSelThreads) {
-        sm.tkey[t] = W.tkey[(int64_t)r * kTieCap + t];
-        sm.tidx[t] = W.tidx[(int64_t)r * kTieCap + t];
+    if (threadIdx.x == 0) {
+      int total = 0, okall = 1;
+      uint32_t kmax = 0u;
+      for (int p = 0; p < g; ++p) {
+        const int32_t* sl = W.slot + ((int64_t)r * kSplitMax + p) * 3;
+        total += sl[0];
+        kmax = max(kmax, (uint32_t)sl[1]);
+        okall &= sl[2];
       }
-      if (threadIdx.x == 0) {
-        sm.ntie = (int)cnt;
-        sm.nout = (int)above;
+      const int X = W.ctr[r] - total;  // start of the row's candidates in its buffer
+      sh_ok = okall && X >= 0 && total >= m && (int64_t)X + total <= SM::kCap ? X : -1;
+      sh_total = total;
+      sh_kmax = kmax;
+      sm.ntie = total;
+      sm.nout = 0;
+    }
+    zero_hist<kSelThreads>(sm, kHistBins);
+    __syncthreads();
+    const int X = sh_ok, total = sh_total;
+    if (X >= 0) {
+      const uint32_t* ck = W.ckey + (int64_t)r * kSelCand + X;
+      const int32_t* ci = W.cidx + (int64_t)r * kSelCand + X;
+      for (int t = threadIdx.x; t < total; t += kSelThreads) {
+        sm.tkey[t] = ck[t];
+        sm.tidx[t] = ci[t];
       }
       __syncthreads();
-      refine_lds<kSelThreads>(2, need, o, sm);
+      const KeyNorm nz = key_norm(W.thr[r], sh_kmax);
+      refine_lds<kSelThreads>(1, (uint32_t)m, o, sm, &nz, true);  // keys normalised over [T, max]
     } else {
-      // tie buffer overflow: redo the whole row in one workgroup (rescan mode)
-      block_select<kSelThreads>(RowSrc{x + off}, n, m, o, sm);
+      block_select<kSelThreads>(RowSrc{xr}, n, m, o, sm);
     }
+    if (threadIdx.x == 0) W.ctr[r] = 0;  // the next call's segments reserve from 0
   }
   for (int j = m + threadIdx.x; j < k; j += kSelThreads) o[j] = -1;
 }
@@ -256,18 +222,11 @@ hipError_t launch_select_single(const float* x, int64_t ld, const int32_t* row_s
 hipError_t launch_select_split(const float* x, int64_t ld, const int32_t* row_start, const int32_t* len,
                                int32_t rows, int32_t k, int32_t g, int32_t* out, void* ws, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  const SplitWs W = carve(ws, rows);
-  const int64_t zero_words = (int64_t)rows * (kHistBins + 2);
-  const int64_t zb = (zero_words + 255) / 256;
-  zero_words_kernel<<<dim3((unsigned)(zb < 1024 ? zb : 1024)), dim3(256), 0, s>>>(W.hist, zero_words);
+  const SegWs W = carve(ws, rows);
+  seg_collect_kernel<<<dim3((unsigned)((int64_t)rows * g)), dim3(kSelThreads), 0, s>>>(x, ld, row_start, len, k, g, W);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((int64_t)rows * g)), block(kSelThreads);
-  mb_hist_kernel<<<grid, block, 0, s>>>(x, ld, row_start, len, k, g, W);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  mb_scatter_kernel<<<grid, block, 0, s>>>(x, ld, row_start, len, k, g, out, W);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  mb_refine_kernel<<<dim3(rows), block, 0, s>>>(x, ld, row_start, len, k, out, W);
+  seg_merge_kernel<<<dim3(rows), dim3(kSelThreads), 0, s>>>(x, ld, row_start, len, k, g, out, W);
   return hipGetLastError();
 }
 

@@ -454,11 +454,17 @@ constexpr int kSelSamples = 2048;
 constexpr int kSelSamplesLong = 6144;
 constexpr int kSelLongRow = 1 << 18;  // rows of at least this many elements take the long sample
 
-// VEC: x is 16-byte aligned and n >= 4 (the 16-byte path; otherwise the 4-byte path only).
-// UV: 16-byte loads per thread and step of the streaming pass (a multiple of 4; a narrow
-// workgroup takes more, to keep as many bytes in flight).
-template <int NT, bool VEC, class SM, int SAMP = kSelSamples, int SEG = 64, int UV = 4>
-__device__ void block_select_sampled(const float* x, int n, int m, int32_t* out, SM& sm) {
+// Steps 1 and 2 for the elements [lo, lo + len) of the row x[0..n): the sample, and so T,
+// is the whole row's whichever segment is streamed, so that every segment of a row keeps
+// the same candidates it would in a whole-row pass.  Leaves the segment's candidates
+// (order key >= T) in sm.tkey / sm.tidx with their row indices, their count in sm.ntie
+// (counting past SM::kCap; only the first kCap are stored), their largest key in sm.kmax,
+// sm.nout = 0 and a zeroed histogram; returns T (0 when the row is no longer than kCap).
+// VEC: x + lo is 16-byte aligned and len >= 4 (the 16-byte path; otherwise the 4-byte path
+// only).  UV: 16-byte loads per thread and step of the streaming pass (a multiple of 4; a
+// narrow workgroup takes more, to keep as many bytes in flight).  Contains barriers.
+template <int NT, bool VEC, class SM, int SAMP, int SEG, int UV>
+__device__ __forceinline__ uint32_t sampled_collect(const float* x, int n, int m, int lo, int len, SM& sm) {
   static_assert(SM::kCap >= SAMP, "the sample lives in the candidate buffer");
   static_assert(SAMP % SEG == 0 && SAMP / SEG >= 2, "whole runs");
   constexpr int NSEG = SAMP / SEG;
@@ -467,8 +473,8 @@ __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out,
   // issued before this step's keys are tested.  The first step's loads do not depend on
   // the threshold, so they are issued before the sample is taken and arrive under it.
   static_assert(UV % 4 == 0, "whole groups of 4 vectors");
-  const float4* xv = reinterpret_cast<const float4*>(x);
-  const int nv = VEC ? n / 4 : 0;  // >= 1 with VEC
+  const float4* xv = reinterpret_cast<const float4*>(x + lo);
+  const int nv = VEC ? len / 4 : 0;  // >= 1 with VEC
   float4 cur[UV], nxt[UV];
   // Unconditional loads (lanes past the end re-read the last vector and are masked when
   // tested): a load under a branch would leave the compiler unable to count the loads in
@@ -502,20 +508,20 @@ __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out,
   }
   lds_sync();
   if (n > SM::kCap) {
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    uint32_t lo_k = 0xFFFFFFFFu, hi_k = 0u;
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       const int t = i * NT + (int)threadIdx.x;
       const uint32_t k = order_key(sv[i]);
       sm.tkey[t] = k;
-      lo = min(lo, k);
-      hi = max(hi, k);
+      lo_k = min(lo_k, k);
+      hi_k = max(hi_k, k);
     }
-    lo = wave_min_u32(lo);
-    hi = wave_max_u32(hi);
+    lo_k = wave_min_u32(lo_k);
+    hi_k = wave_max_u32(hi_k);
     if (l == 0) {
-      atomicMin(&sm.kmin, lo);
-      atomicMax(&sm.kmax, hi);
+      atomicMin(&sm.kmin, lo_k);
+      atomicMax(&sm.kmax, hi_k);
     }
     zero_hist<NT>(sm, kHistBins);  // the sample's radix level, cleared under the same barrier
     lds_sync();
@@ -580,7 +586,7 @@ __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out,
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           ok[4 * u + c] = jv < nv;
-          ix_[4 * u + c] = 4 * jv + c;
+          ix_[4 * u + c] = lo + 4 * jv + c;
         }
       }
       append(k_, ok, ix_, std::integral_constant<int, 16>{});
@@ -588,25 +594,35 @@ __device__ void block_select_sampled(const float* x, int n, int m, int32_t* out,
 #pragma unroll
     for (int u = 0; u < UV; ++u) cur[u] = nxt[u];
   }
-  // Scalar part: the rest (all of the row when it is not 16-byte aligned), loads clamped
-  // like the vector part's.
+  // Scalar part: the rest (all of the segment when it is not 16-byte aligned), loads
+  // clamped like the vector part's.
   constexpr int U = 8;
-  for (int base = nv * 4; base < n; base += U * NT) {
+  const float* xs = x + lo;
+  for (int base = nv * 4; base < len; base += U * NT) {
     uint32_t k_[U];
     bool ok[U];
     int ix_[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = base + u * NT + (int)threadIdx.x;
-      ok[u] = j < n;
-      k_[u] = order_key(x[ok[u] ? j : n - 1]);
-      ix_[u] = j;
+      ok[u] = j < len;
+      k_[u] = order_key(xs[ok[u] ? j : len - 1]);
+      ix_[u] = lo + j;
     }
     append(k_, ok, ix_, std::integral_constant<int, U>{});
   }
   kmax = wave_max_u32(kmax);
   if (l == 0 && kmax) atomicMax(&sm.kmax, kmax);
   __syncthreads();
+  return T;
+}
+
+// Top-m of a materialised row x[0..n) (1 <= m < n): sampled_collect() over the whole row,
+// then the LDS refinement of its candidates, or the exact multi-pass block_select() when
+// the sample misjudged the row.  VEC and UV as for sampled_collect().
+template <int NT, bool VEC, class SM, int SAMP = kSelSamples, int SEG = 64, int UV = 4>
+__device__ void block_select_sampled(const float* x, int n, int m, int32_t* out, SM& sm) {
+  const uint32_t T = sampled_collect<NT, VEC, SM, SAMP, SEG, UV>(x, n, m, 0, n, sm);
   const int c = sm.ntie;
   const KeyNorm nz = key_norm(T, sm.kmax);
   __syncthreads();

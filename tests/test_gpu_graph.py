@@ -88,7 +88,8 @@ def test_fused_topk_noalloc_graph_replays(family):
 @pytest.mark.parametrize("split", [0, 4])
 def test_score_and_select_graph_replays(split):
     """idx_score then idx_select (the dense route) captured together; the row-split select
-    clears its histograms with a kernel of its own, which must also replay correctly."""
+    keeps per-row counters in its workspace that each call leaves at zero for the next, so
+    every replay must find them so."""
     p = wl.long_context(rows=16, num_keys=200000, band_keys=3000, topk=2048, seed=104)
     dp = sai.DeviceProblem.from_host(p)
     V = torch.from_numpy((p.ke - p.ks).astype(np.int32)).cuda()

@@ -289,6 +289,35 @@ def test_select_sampled_rows_ragged_and_unaligned(split):
     assert_same_sets(got, ref, f"split={split}")
 
 
+@pytest.mark.parametrize("split", [2, 3, 7, 32])
+def test_select_row_split_routes(split):
+    """The row split (several workgroups per row, each appending its segment's candidates to
+    the row's buffer; one workgroup per row refines them) on rows that take each of its
+    routes: long rows with a planted band of high runs (refinement), one whose top values
+    fill its last quarter (a segment overflows: exact multi-pass route), one whose sample
+    holds the only large values (fewer candidates than k: exact route), rows shorter than
+    the split length and with n <= k (selected whole), and an empty row.  The workspace
+    starts filled with garbage, so the first call finds the per-row counters unset (rows
+    then take the exact route); the second call finds them at zero.  Both equal the oracle."""
+    rng = np.random.default_rng(40 + split)
+    ld, k = 131072, 2048
+    x = rng.normal(0.0, 0.05, size=(8, ld)).astype(np.float32)
+    for r in (0, 1):
+        for _ in range(80):
+            a = int(rng.integers(0, ld - 32))
+            x[r, a:a + 32] = (1.0 + 0.1 * rng.standard_normal(32)).astype(np.float32)
+    x[2, 3 * ld // 4:] = np.float32(2.0)
+    pos = _sample_positions(ld)
+    x[3, pos[:300]] = 1.0 + rng.uniform(0, 1e-3, size=300).astype(np.float32)
+    n = np.array([ld, ld - 5, ld, ld, 16383, 20000, k, 0], dtype=np.int32)
+    ref = oracle.select_rows(x, n, k)
+    run = sai.SelectRunner(torch.from_numpy(x).cuda(), torch.from_numpy(n).cuda(), k, split=split)
+    run.ws.fill_(0xA5)
+    for call in range(2):
+        got = run().cpu().numpy()
+        assert_same_sets(got, ref, f"split={split}, call {call}")
+
+
 def test_select_row_start_offsets():
     rng = np.random.default_rng(4)
     x = rng.standard_normal((4, 5000)).astype(np.float32)
