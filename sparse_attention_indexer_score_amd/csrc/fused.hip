@@ -83,6 +83,8 @@ struct EpiArgs {
   int32_t skip_le;  // SAMPLE: rows with ke - ks <= skip_le need no samples
   // ROWSTORE
   int32_t only_row;
+  // paged FILTER: persistent workgroups take their items after the first by this ticket
+  int32_t* ticket;
 };
 
 struct TileWork {
@@ -91,10 +93,11 @@ struct TileWork {
   int32_t chunk;   // positions per chunk (multiple of kTile)
   int32_t spread;  // 1: every chunk's row blocks are dealt over all XCDs (keys private to a row block)
   int64_t total;   // nrb * nchunk
+  int64_t grid;    // workgroups when each takes one item (the mapping's virtual grid)
 };
 
-// Workgroup -> work item (item = chunk * nrb + row block).  Workgroups are dealt to the 8
-// XCDs round-robin, so workgroup b runs on XCD b % 8.
+// Workgroup b -> work item (item = chunk * nrb + row block), for b < W.grid.  Workgroups are
+// dealt to the 8 XCDs round-robin, so workgroup b runs on XCD b % 8.
 //  - At least 8 chunks: chunk c runs on XCD c % 8, its row blocks back to back, so its keys
 //    are fetched into that XCD's L2 once and the chunks near the start of the key range,
 //    which short rows still reach, are spread over all XCDs.  Grid: ceil(nchunk / 8) * 8
@@ -105,8 +108,7 @@ struct TileWork {
 //    The chunk groups are dealt last first.  Same grid.
 //  - Fewer chunks: XCD x takes the x-th eighth of the items, so every XCD has work.  Grid:
 //    8 * ceil(total / 8) workgroups.
-__device__ __forceinline__ int64_t map_item(const TileWork& W) {
-  const int64_t b = blockIdx.x;
+__device__ __forceinline__ int64_t map_item(const TileWork& W, int64_t b) {
   const int64_t x = b & 7, local = b >> 3;
   if (W.nchunk < 8) return x * ((W.total + 7) / 8) + local;
   int64_t g = local / W.nrb;
@@ -869,7 +871,7 @@ __global__ __launch_bounds__(kThreads, 2) void score_tiles_kernel(ScoreArgs A, L
   constexpr int RW = RowsPerWave<FMT, H>::value;
   __shared__ StageShared<FMT> sh;
   __shared__ CandShared<RW, MODE == MODE_FILTER> cand;
-  const int64_t item = map_item(W);
+  const int64_t item = map_item(W, blockIdx.x);
   if (item >= W.total) return;
   const int rb = (int)(item % W.nrb);
   const int chunk = (int)(item / W.nrb);
@@ -904,72 +906,92 @@ __device__ __forceinline__ int request_of(const ScoreArgs& A, int r) {
   return q < 0 ? 0 : (q >= A.num_req ? A.num_req - 1 : q);
 }
 
-// Paged keys: one workgroup per (row quad, key chunk).  Rows must read one request's pages
+// Paged keys: one work item per (row quad, key chunk).  Rows must read one request's pages
 // to share the LDS stage.  When all four rows belong to one request (MTP decode rows), the
 // two row pairs share each stage: waves 0/1 hold the pairs and take even tiles, waves 2/3
 // the odd ones.  Otherwise each pair is scored on its own with all four waves holding it,
 // and a pair that straddles two requests in two one-row passes.
+// The FILTER launch with a ticket counter runs persistent workgroups (two per CU): each
+// takes item map_item(b) for its own index b first, then b = grid size + the ticket it drew
+// while scoring the previous item, until b reaches the virtual grid.  Every b is taken
+// once, empty items (chunks past every row's keys, most of a decode batch) cost a loop
+// turn instead of a workgroup launch, and the workgroups that finish early take the
+// remaining items.
 template <int FMT, int H, int MODE>
 __global__ __launch_bounds__(kThreads, 2) void score_pages_kernel(ScoreArgs A, LinArgs L, EpiArgs E, TileWork W) {
   __shared__ StageShared<FMT> sh;
   __shared__ CandShared<2, MODE == MODE_FILTER> cand;
   __shared__ int32_t pages[kPageCache];
-  const int64_t item = map_item(W);
-  if (item >= W.total) return;
-  const int rb = (int)(item % W.nrb);
-  const int chunk = (int)(item / W.nrb);
-  const int base = 4 * rb;
-  const int S = (MODE == MODE_SAMPLE) ? E.stride : 1;
-  const int phase = (MODE == MODE_SAMPLE) ? sample_phase(rb, S) : 0;
-  const int c0 = chunk * W.chunk, c1 = c0 + W.chunk;
-  const int wave = uniform(threadIdx.x / kWave);
-  const StageLds<FMT> sl{sh.codes, sh.sf, sh.ks, cand.s, cand.i, pages};
-  // Tile range of the given rows within the chunk (positions: keys or sample slots).
-  auto span = [&](int r0, int n, uint32_t rmask, int& tA, int& tB, int& kmax) {
-    int lo = 0x7FFFFFFF, hi = 0;
-    kmax = 0;
-    for (int i = 0; i < n; ++i) {
-      const int r = r0 + i;
-      if (r >= A.rows || !((rmask >> i) & 1)) continue;
-      const int ks = A.ks[r], ke = A.ke[r];
-      kmax = max(kmax, ke - 1);
-      int plo = ks, phi = ke;
-      if (MODE == MODE_SAMPLE) {
-        plo = phi = 0;
-        if (ke - ks > E.skip_le) sample_range(ks, ke, phase, S, plo, phi);
-      }
-      if (phi > plo) {
-        lo = min(lo, plo);
-        hi = max(hi, phi);
+  __shared__ int sh_next;
+  const bool persistent = MODE == MODE_FILTER && E.ticket != nullptr;
+  for (int64_t b = blockIdx.x; b < W.grid;) {  // workgroup-uniform
+    int next = 0;
+    // drawn now and used after the item, so that the atomic's round trip hides under it
+    if (persistent && threadIdx.x == 0) next = atomicAdd(E.ticket, 1);
+    const int64_t item = map_item(W, b);
+    if (item < W.total) {
+      const int rb = (int)(item % W.nrb);
+      const int chunk = (int)(item / W.nrb);
+      const int base = 4 * rb;
+      const int S = (MODE == MODE_SAMPLE) ? E.stride : 1;
+      const int phase = (MODE == MODE_SAMPLE) ? sample_phase(rb, S) : 0;
+      const int c0 = chunk * W.chunk, c1 = c0 + W.chunk;
+      const int wave = uniform(threadIdx.x / kWave);
+      const StageLds<FMT> sl{sh.codes, sh.sf, sh.ks, cand.s, cand.i, pages};
+      // Tile range of the given rows within the chunk (positions: keys or sample slots).
+      auto span = [&](int r0, int n, uint32_t rmask, int& tA, int& tB, int& kmax) {
+        int lo = 0x7FFFFFFF, hi = 0;
+        kmax = 0;
+        for (int i = 0; i < n; ++i) {
+          const int r = r0 + i;
+          if (r >= A.rows || !((rmask >> i) & 1)) continue;
+          const int ks = A.ks[r], ke = A.ke[r];
+          kmax = max(kmax, ke - 1);
+          int plo = ks, phi = ke;
+          if (MODE == MODE_SAMPLE) {
+            plo = phi = 0;
+            if (ke - ks > E.skip_le) sample_range(ks, ke, phase, S, plo, phi);
+          }
+          if (phi > plo) {
+            lo = min(lo, plo);
+            hi = max(hi, phi);
+          }
+        }
+        tA = max(c0, lo) / kTile;
+        tB = (min(c1, hi) + kTile - 1) / kTile;
+      };
+      const int nr = min(4, A.rows - base);
+      bool one_req = nr == 4;
+      for (int i = 1; i < nr && one_req; ++i) one_req = request_of(A, base + i) == request_of(A, base);
+      if (one_req) {
+        int tA, tB, kmax;
+        span(base, 4, 0xFu, tA, tB, kmax);
+        if (tA < tB)
+          wg_tiles<FMT, H, MODE, 2, true>(A, L, E, base + 2 * (wave & 1), phase, S, c0, c1, tA, tB, sl,
+                                          request_of(A, base), ~0u, 2, wave >> 1, kmax);
+      } else {
+        for (int pr = 0; pr < 2; ++pr) {  // workgroup-uniform
+          const int row0 = base + 2 * pr;
+          if (row0 >= A.rows) break;
+          const bool two = row0 + 1 < A.rows;
+          const int q0 = request_of(A, row0), q1 = two ? request_of(A, row0 + 1) : q0;
+          for (int pass = 0; pass < (q0 == q1 ? 1 : 2); ++pass) {
+            const uint32_t rmask = q0 == q1 ? 3u : (1u << pass);
+            int tA, tB, kmax;
+            span(row0, 2, rmask, tA, tB, kmax);
+            if (tA < tB)
+              wg_tiles<FMT, H, MODE, 2, true>(A, L, E, row0, phase, S, c0, c1, tA, tB, sl, pass == 0 ? q0 : q1,
+                                              rmask);
+            __syncthreads();
+          }
+        }
       }
     }
-    tA = max(c0, lo) / kTile;
-    tB = (min(c1, hi) + kTile - 1) / kTile;
-  };
-  const int nr = min(4, A.rows - base);
-  bool one_req = nr == 4;
-  for (int i = 1; i < nr && one_req; ++i) one_req = request_of(A, base + i) == request_of(A, base);
-  if (one_req) {
-    int tA, tB, kmax;
-    span(base, 4, 0xFu, tA, tB, kmax);
-    if (tA < tB)
-      wg_tiles<FMT, H, MODE, 2, true>(A, L, E, base + 2 * (wave & 1), phase, S, c0, c1, tA, tB, sl,
-                                      request_of(A, base), ~0u, 2, wave >> 1, kmax);
-    return;
-  }
-  for (int pr = 0; pr < 2; ++pr) {  // workgroup-uniform
-    const int row0 = base + 2 * pr;
-    if (row0 >= A.rows) break;
-    const bool two = row0 + 1 < A.rows;
-    const int q0 = request_of(A, row0), q1 = two ? request_of(A, row0 + 1) : q0;
-    for (int pass = 0; pass < (q0 == q1 ? 1 : 2); ++pass) {
-      const uint32_t rmask = q0 == q1 ? 3u : (1u << pass);
-      int tA, tB, kmax;
-      span(row0, 2, rmask, tA, tB, kmax);
-      if (tA < tB)
-        wg_tiles<FMT, H, MODE, 2, true>(A, L, E, row0, phase, S, c0, c1, tA, tB, sl, pass == 0 ? q0 : q1, rmask);
-      __syncthreads();
-    }
+    if (!persistent) break;
+    if (threadIdx.x == 0) sh_next = next;
+    __syncthreads();  // (also: the item's LDS is free for the next)
+    b = (int64_t)gridDim.x + sh_next;
+    __syncthreads();
   }
 }
 
@@ -1372,13 +1394,11 @@ static TileWork tile_work(const DevProblem& P, int64_t positions, int chunk) {
   if (W.nchunk < 1) W.nchunk = 1;
   W.spread = P.page_table != nullptr;
   W.total = (int64_t)W.nrb * W.nchunk;
+  W.grid = W.nchunk < 8 ? 8 * ((W.total + 7) / 8) : (int64_t)((W.nchunk + 7) / 8) * 8 * W.nrb;
   return W;
 }
 
-static dim3 tile_grid(const TileWork& W) {
-  if (W.nchunk < 8) return dim3((unsigned)(8 * ((W.total + 7) / 8)));
-  return dim3((unsigned)((W.nchunk + 7) / 8 * 8 * W.nrb));
-}
+static dim3 tile_grid(const TileWork& W) { return dim3((unsigned)W.grid); }
 
 static LinArgs lin_args(const FusedPlan& F) { return LinArgs{F.lin_q8, F.lin_sf}; }
 
@@ -1398,9 +1418,11 @@ static hipError_t launch_lin_prep(const DevProblem& P, uint8_t* q8, uint8_t* sf,
 
 template <int MODE>
 static hipError_t dispatch_score(const DevProblem& P, const LinArgs& L, const EpiArgs& E, const TileWork& W,
-                                 hipStream_t s) {
+                                 hipStream_t s, int64_t max_groups = 0) {
   const ScoreArgs A = score_args(P);
-  const dim3 grid = tile_grid(W), block(kThreads);
+  dim3 grid = tile_grid(W);  // (persistent paged FILTER: at most max_groups, the rest by ticket)
+  if (max_groups > 0 && grid.x > max_groups) grid.x = (unsigned)max_groups;
+  const dim3 block(kThreads);
   if (P.page_table) {  // paged keys are e4m3 (checked at the boundary)
     if (P.heads == 64) score_pages_kernel<FMT_E4M3, 64, MODE><<<grid, block, 0, s>>>(A, L, E, W);
     else score_pages_kernel<FMT_E4M3, 32, MODE><<<grid, block, 0, s>>>(A, L, E, W);
@@ -1530,7 +1552,12 @@ hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_id
     E.slab_s = F.slab_s;
     E.slab_i = F.slab_i;
     E.cap = F.cap;
-    if ((e = dispatch_score<MODE_FILTER>(P, L, E, tile_work(P, P.key_span, chunk_keys(P)), s)) != hipSuccess)
+    int64_t groups = 0;
+    if (P.page_table) {  // persistent: two workgroups per CU (ticket cleared by K1b)
+      E.ticket = F.fb_ctrl + kPagedTicketWord;
+      groups = 2 * (int64_t)F.cu;
+    }
+    if ((e = dispatch_score<MODE_FILTER>(P, L, E, tile_work(P, P.key_span, chunk_keys(P)), s, groups)) != hipSuccess)
       return e;
     if ((e = mark(3)) != hipSuccess) return e;
   }

@@ -26,9 +26,11 @@ struct DevProblem {
 
 // Exact fallback: scratch rows (queued rows re-scored at once) and the control words ahead
 // of the queued-row list: [0] queued count, [1] head of the rows past the scratch rows,
-// [2, 2 + kFbSlots) chunks scored so far of each scratch row's row.
+// [2, 2 + kFbSlots) chunks scored so far of each scratch row's row; then the ticket counter
+// of the paged score + filter kernel's persistent workgroups.
 constexpr int kFbSlots = 32;
-constexpr int kFbCtrlWords = 2 + kFbSlots;
+constexpr int kFbCtrlWords = 2 + kFbSlots + 1;
+constexpr int kPagedTicketWord = 2 + kFbSlots;
 
 // Per-call plan of the fused path (sizes and workspace carve-up).
 struct FusedPlan {
