@@ -108,13 +108,19 @@ __device__ __forceinline__ void segment(int n, int g, int part, int& lo, int& hi
   hi = min(n, lo + seg);
 }
 
+// Workgroup b runs on XCD b % 8 (workgroups are dealt to the XCDs round-robin): row r's g
+// segments are workgroups 8 (g (r / 8) + part) + r % 8, all on XCD r % 8, so that the
+// row's sample, which every segment reads, is fetched into one L2 once.  Grid: 8 g
+// ceil(rows / 8).
 __global__ __launch_bounds__(kSelThreads, 8) void seg_collect_kernel(const float* x, int64_t ld,
                                                                     const int32_t* row_start, const int32_t* len,
-                                                                    int32_t k, int32_t g, SegWs W) {
+                                                                    int32_t rows, int32_t k, int32_t g, SegWs W) {
   using SM = SelSmemT<kSelCand>;
   __shared__ SM sm;
   __shared__ int sh_pos;
-  const int r = blockIdx.x / g, part = blockIdx.x % g;
+  const int local = (int)(blockIdx.x >> 3), part = local % g;
+  const int r = (local / g) * 8 + (int)(blockIdx.x & 7);
+  if (r >= rows) return;
   int n, m;
   const int64_t off = row_span(ld, row_start, len, r, k, n, m);
   if (m >= n) return;  // the merge kernel writes such rows whole
@@ -223,7 +229,8 @@ hipError_t launch_select_split(const float* x, int64_t ld, const int32_t* row_st
                                int32_t rows, int32_t k, int32_t g, int32_t* out, void* ws, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const SegWs W = carve(ws, rows);
-  seg_collect_kernel<<<dim3((unsigned)((int64_t)rows * g)), dim3(kSelThreads), 0, s>>>(x, ld, row_start, len, k, g, W);
+  const int64_t groups = 8 * (int64_t)g * ((rows + 7) / 8);
+  seg_collect_kernel<<<dim3((unsigned)groups), dim3(kSelThreads), 0, s>>>(x, ld, row_start, len, rows, k, g, W);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   seg_merge_kernel<<<dim3(rows), dim3(kSelThreads), 0, s>>>(x, ld, row_start, len, k, g, out, W);
