@@ -22,6 +22,8 @@ FAMILIES = {
     "long_mxfp4_32h": lambda: wl.long_context(rows=48, num_keys=40000, band_keys=3000, topk=512, seed=101),
     "prefill_e4m3_64h": lambda: wl.prefill(rows=40, num_keys=20000, topk=1024, seed=102),
     "decode_paged": lambda: wl.decode(num_req=12, ctx_lo=4000, ctx_hi=60000, topk=2048, seed=103),
+    # enough work items that the paged filter's persistent workgroups take most by ticket
+    "decode_paged_tickets": lambda: wl.decode(num_req=40, ctx_lo=8192, ctx_hi=262144, topk=2048, seed=105),
 }
 
 

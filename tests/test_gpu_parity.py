@@ -189,6 +189,15 @@ def test_paged_row_pairs_straddling_requests():
     assert st["rows_store_all"] + st["rows_sampled"] == p.rows
 
 
+def test_decode_persistent_workgroups():
+    """A decode batch large enough that the paged score + filter launch takes most of its work
+    items by ticket: 40 requests of up to 262,144 keys give 64 key chunks x 40 row quads,
+    against two persistent workgroups per CU."""
+    p = wl.decode(num_req=40, ctx_lo=8192, ctx_hi=262144, seed=19)
+    st = full_check(p, 2048, score_rows=[0, p.rows - 1])
+    assert st["rows_store_all"] + st["rows_sampled"] == p.rows
+
+
 # ----------------------------------------------------------------------------- edges
 
 @pytest.mark.parametrize("k", [1, 7, 100, 1000, 2048])
