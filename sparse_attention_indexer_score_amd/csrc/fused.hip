@@ -829,7 +829,10 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
         }
       }
     } else {
-#pragma unroll
+      // Stages that are not whole (a chunk's first and last, and where rows end) are few: a
+      // rolled loop keeps one copy of the tile code and its candidate flushes instead of
+      // kTiles, a third of the kernel's code.
+#pragma nounroll
       for (int i = 0; i < G::kTiles; ++i) {
         const int t = tbase + i;
         if (t >= tB) break;  // workgroup-uniform
