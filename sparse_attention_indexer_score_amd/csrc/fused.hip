@@ -828,11 +828,19 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
           epilogue(tbase + i, sc, true);
         }
       }
-    } else {
-      // Stages that are not whole (a chunk's first and last, and where rows end) are few: a
-      // rolled loop keeps one copy of the tile code and its candidate flushes instead of
-      // kTiles, a third of the kernel's code.
+    } else if constexpr (kWhole) {
+      // With the whole-stage loop above, the stages that reach this loop (a chunk's first and
+      // last, and where rows end) are few: rolled, it keeps one copy of the tile code and its
+      // candidate flushes instead of kTiles, a third of the kernel's code.
 #pragma nounroll
+      for (int i = 0; i < G::kTiles; ++i) {
+        const int t = tbase + i;
+        if (t >= tB) break;  // workgroup-uniform
+        const bool mine = SHARED ? ((i % split) == (slot < 0 ? wave : slot)) : (t >= wt0 && t < wt1);
+        if (mine) compute(sbase, i, t, false);
+      }
+    } else {
+#pragma unroll
       for (int i = 0; i < G::kTiles; ++i) {
         const int t = tbase + i;
         if (t >= tB) break;  // workgroup-uniform
