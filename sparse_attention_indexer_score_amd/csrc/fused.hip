@@ -383,21 +383,50 @@ __device__ __forceinline__ float relu_bits(float x) { return clamp0(x); }
 // Key tiles are staged through LDS: all four waves of a workgroup use the same keys, so a
 // stage of 32-key tiles is fetched once per workgroup with 16-byte loads straight into LDS
 // (issued one stage ahead, double-buffered, one barrier per stage) and each wave reads its
-// MFMA key operands from LDS.  Rows are padded to KB + 16 bytes so that the 8 lanes of a 16-byte LDS
-// read phase hit distinct banks.  A stage is 8 tiles of 80-byte fp4 rows or 4 tiles of
-// 144-byte e4m3 rows, which keeps two workgroups per CU within LDS.
+// MFMA key operands from LDS.  A 16-byte LDS read phase takes 8 (or 16) lanes, i.e. 8 (16)
+// consecutive keys at the same 16-byte part, which the layout puts in distinct banks.
+// fp4: one region per K-step, [ks][key][32 bytes], the two 16-byte halves of key k's row
+// swapped when g(k) = 1, so that a stage is a dense copy of its keys in another order: a
+// lane's load offset is the same in every stage, and K-step 1 sits a constant distance
+// from K-step 0.  e4m3: rows padded to 144 bytes (a row stride of 9 parts).  A stage is 8
+// fp4 tiles (16 KB) or 4 e4m3 tiles (18 KB), which keeps two workgroups per CU within LDS.
 template <int FMT>
 struct StageGeom {
+  static constexpr bool kSwz = FMT == FMT_MXFP4;            // K-step regions (else padded rows)
   static constexpr int kTiles = FMT == FMT_MXFP4 ? 8 : 4;  // tiles per stage
   static constexpr int kKB = Fmt<FMT>::kBytes;
-  static constexpr int kStride = kKB + 16;
+  static constexpr int kParts = kKB / 16;                   // 16-byte parts of a key
   static constexpr int kKeys = kTiles * kTile;             // keys per stage
-  static constexpr int kBytes = kKeys * kStride;           // codes of one stage
+  static constexpr int kRow = kSwz ? kKB / 2 : kKB + 16;    // bytes per LDS row
+  static constexpr int kSlotsPerRow = kRow / 16;
+  static constexpr int kBytes = kKeys * (kSwz ? kKB : kRow);  // codes of one stage
+  static constexpr int kStepOff = kSwz ? kKeys * kRow : 64;   // K-step 1 from K-step 0
+  // Half swap of stage key k (k mod 16 decides: stage and tile starts are multiples of 16
+  // keys).  Keys k and k + 4 of an 8-key phase share banks otherwise (32-byte rows over 128
+  // bytes of banks), as do keys k and k + 8 of a 16-key phase over 256 bytes.
+  static __device__ __forceinline__ int g(int k) { return ((k >> 2) ^ (k >> 3)) & 1; }
+  // Byte offset of lane (col, half)'s K-step 0 part within a tile.
+  static __device__ __forceinline__ int lane_off(int col, int half) {
+    if constexpr (kSwz) return col * kRow + ((half ^ g(col)) * 16);
+    else return col * kRow + half * 32;
+  }
+  // Key and part that LDS slot sidx of a stage holds (pad slots: part 0 of their key again).
+  static __device__ __forceinline__ int slot_key(int sidx) {
+    if constexpr (kSwz) return (sidx % (2 * kKeys)) / 2;
+    else return sidx / kSlotsPerRow;
+  }
+  static __device__ __forceinline__ int slot_part(int sidx) {
+    if constexpr (kSwz) return 2 * (sidx / (2 * kKeys)) + ((sidx & 1) ^ g(slot_key(sidx)));
+    else {
+      const int part = sidx % kSlotsPerRow;
+      return part < kParts ? part : 0;
+    }
+  }
 };
 
 template <int FMT>
 struct StageLds {
-  uint8_t* codes;  // [2][kKeys * kStride]
+  uint8_t* codes;  // [2][kBytes]
   uint32_t* sf;    // [2][kKeys] e8m0 words (MXFP4)
   float* ks;       // [2][kKeys] per-key scale (1.0 when absent)
   float* cand_s;   // FILTER: [waves][RW][kCandBuf] candidate scores of this workgroup's rows
@@ -631,21 +660,20 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
       asm volatile("" : "+v"(a));
       return (lds_ptr)(uintptr_t)a;
     };
-    constexpr int kHalfOff = FMT == FMT_E4M3 ? 32 : 16;
-    return StageBase{opaque(sl.codes + buf * G::kBytes + col * G::kStride + half * kHalfOff),
+    return StageBase{opaque(sl.codes + buf * G::kBytes + G::lane_off(col, half)),
                      opaque(sl.sf + buf * G::kKeys + col), opaque(sl.ks + buf * G::kKeys + col)};
   };
   // Key operand and half key scale of tile slot i of the stage at `sb`.
   auto read_b = [&](const StageBase& sb, int i, KeyOperand& ko, float& kscale) {
-    lds_ptr row = sb.codes + i * kTile * G::kStride;
+    lds_ptr row = sb.codes + i * kTile * G::kRow;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       if constexpr (FMT == FMT_E4M3) {
-        const v4i x0 = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(row + ks * 64);
-        const v4i x1 = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(row + ks * 64 + 16);
+        const v4i x0 = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(row + ks * G::kStepOff);
+        const v4i x1 = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(row + ks * G::kStepOff + 16);
         ko.b[ks] = v8i{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
       } else {
-        const v4i x = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(row + ks * 32);
+        const v4i x = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(row + ks * G::kStepOff);
         ko.b[ks] = v8i{x.x, x.y, x.z, x.w, 0, 0, 0, 0};
       }
     }
@@ -709,10 +737,9 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
 
   // Stage loads straight into LDS (global_load_lds_dwordx4): lane l of wave w writes the 16
   // bytes it fetches to the wave's LDS base + 16 l, so each lane is given the global piece
-  // that belongs in its 16-byte slot of the padded [key][kStride] layout (a pad slot fetches
-  // part 0 of its key again).  Block scales and key scales come by 4-byte loads.
-  constexpr int kSlotsPerKey = G::kStride / 16;
-  constexpr int kSlots = G::kKeys * kSlotsPerKey;
+  // that belongs in its 16-byte slot of the stage layout (G::slot_key, G::slot_part).
+  // Block scales and key scales come by 4-byte loads.
+  constexpr int kSlots = G::kBytes / 16;
   constexpr int kSlotIters = (kSlots + kThreads - 1) / kThreads;
   const bool has_ks = A.k_scale != nullptr;
   // LDS destination of a stage load, as an address the compiler cannot trace to a variable.
@@ -726,9 +753,10 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
     const int64_t pos0 = (int64_t)(tA + stage * G::kTiles) * kTile;
     uint8_t* lbase = sl.codes + buf * G::kBytes;
     int ln = l;
-    // Paged stages: the lane-derived slot offsets are recomputed per stage rather than held
-    // in registers, which the 64-head kernels would otherwise spill.
-    if constexpr (SHARED) asm volatile("" : "+v"(ln));
+    // Paged and sampled stages: the lane-derived slot offsets are recomputed per stage
+    // rather than held in registers, which the 64-head paged and the 4-row sample kernels
+    // would otherwise spill.
+    if constexpr (SHARED || MODE == MODE_SAMPLE) asm volatile("" : "+v"(ln));
     {
       // Paged with the page ids in LDS: key_of in 32-bit arithmetic when every position the
       // stages reach, times the stride, stays below 2^31.
@@ -739,9 +767,9 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
           const int s0 = u * kThreads + wave * kWave;
           if (s0 < kSlots) {
             const int sidx = s0 + ln;
-            const int key = min(phase + (kpos0 + sidx / kSlotsPerKey) * S, lmax), part = sidx % kSlotsPerKey;
+            const int key = min(phase + (kpos0 + G::slot_key(sidx)) * S, lmax);
             const int32_t id = sl.pages[(key >> 6) - pbase];
-            const int32_t off = (key & (kPage - 1)) * KB + (part < KB / 16 ? part : 0) * 16;
+            const int32_t off = (key & (kPage - 1)) * KB + G::slot_part(sidx) * 16;
             __builtin_amdgcn_global_load_lds(
                 (const __attribute__((address_space(1))) void*)(A.k + (int64_t)id * (kPage * KB) + off),
                 lds_dst(lbase + s0 * 16), 16, 0, 0);
@@ -760,14 +788,41 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
         return;
       }
     }
+    if constexpr (G::kSwz && MODE != MODE_SAMPLE) {  // sample positions are strided
+      // Contiguous keys with the whole stage inside the key array: the stage holds the 64-byte
+      // rows of kKeys consecutive keys, so a lane's source is the stage's first key plus an
+      // offset of its own.  Load u fills K-step u / 2 of keys [128 (u % 2), +128); a wave's
+      // 64 slots there are 32 whole keys, 16-key aligned, so the half swap depends on the
+      // lane alone.  The lane offset is formed anew in each stage (no register held across
+      // the tile loop) and added to a wave-uniform base.
+      const int64_t kfirst = (int64_t)phase + pos0;
+      if (req < 0 && S == 1 && kfirst + G::kKeys - 1 <= last_key) {  // wave-uniform
+        static_assert(kSlots == 4 * kThreads && G::kKeys == 2 * 128, "four loads of 128 keys' K-step halves");
+        int lv = l;
+        asm volatile("" : "+v"(lv));
+        const int kq = lv >> 1;
+        const uint32_t loff = (uint32_t)(kq * KB + (((lv & 1) ^ G::g(kq)) * 16));
+        const uint8_t* gb = A.k + kfirst * KB + wave * (kWave / 2) * KB;
+#pragma unroll
+        for (int u = 0; u < kSlotIters; ++u)
+          __builtin_amdgcn_global_load_lds(
+              (const __attribute__((address_space(1))) void*)(gb + (loff + (uint32_t)((u & 1) * 128 * KB + (u >> 1) * (KB / 2)))),
+              lds_dst(lbase + (u * kThreads + wave * kWave) * 16), 16, 0, 0);
+        const int64_t gk = kfirst + wave * kWave;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(A.k_sf + gk * 4 + (uint32_t)(lv * 4)),
+                                         lds_dst(sl.sf + buf * G::kKeys + wave * kWave), 4, 0, 0);
+        if (has_ks)
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(A.k_scale + gk + (uint32_t)lv),
+                                           lds_dst(sl.ks + buf * G::kKeys + wave * kWave), 4, 0, 0);
+        return;
+      }
+    }
 #pragma unroll
     for (int u = 0; u < kSlotIters; ++u) {
       const int s0 = u * kThreads + wave * kWave;
       if (s0 < kSlots) {  // wave-uniform
         const int sidx = s0 + ln;
-        const int key = sidx / kSlotsPerKey, part = sidx % kSlotsPerKey;
-        const int pp = part < KB / 16 ? part : 0;
-        const uint8_t* src = A.k + key_of(pos0 + key) * KB + pp * 16;
+        const uint8_t* src = A.k + key_of(pos0 + G::slot_key(sidx)) * KB + G::slot_part(sidx) * 16;
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                          lds_dst(lbase + s0 * 16), 16, 0, 0);
       }
