@@ -328,12 +328,13 @@ __device__ __forceinline__ void load_lin(LinOperand& lo, const LinArgs& L, int r
   const int m = l & 31, half = l >> 5;
   const int s = 4 * (m >> 3) + (m & 3), hh = (m >> 2) & 1;
   const int p = s / kPieces, c = s % kPieces;
-  const int row = row0 + 2 * p + hh;
+  const int row = row0 + 2 * p + (c == 1 ? 1 : c == 0 ? 0 : hh);
+  const int piece = c < 2 ? hh : c;
   const bool ok = p < npairs && row < rows;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     if (ok) {
-      const int64_t base = (((int64_t)row * kPieces + c) * 2 + ks) * 2 + half;
+      const int64_t base = (((int64_t)row * kPieces + piece) * 2 + ks) * 2 + half;
       const v4i x0 = *reinterpret_cast<const v4i*>(L.q8 + base * 32);
       const int2 x1 = *reinterpret_cast<const int2*>(L.q8 + base * 32 + 16);
       lo.a[ks] = v8i{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, 0, 0};
@@ -342,7 +343,7 @@ __device__ __forceinline__ void load_lin(LinOperand& lo, const LinArgs& L, int r
     }
   }
   if (ok) {
-    const int64_t b0 = (((int64_t)row * kPieces + c) * 2) * 2 + half;  // K-step 0; K-step 1 is b0 + 2
+    const int64_t b0 = (((int64_t)row * kPieces + piece) * 2) * 2 + half;  // K-step 0; K-step 1 is b0 + 2
     lo.sa = (int)L.sf[b0] | ((int)L.sf[b0 + 2] << 8);
   } else {
     lo.sa = 0x7F7F;
@@ -358,11 +359,14 @@ __device__ __forceinline__ v16f mfma_lin(const LinOperand& lo, const KeyOperand&
   return a;
 }
 
-__device__ __forceinline__ float lin_of_pair(const v16f& a, int p) {
-  const int s = kPieces * p;
-  float x = a[s];
+// Start value of row r's head sum on this lane half (pieces 0 and 1 of the row, one per
+// half, so that the half-wave combine adds them).
+__device__ __forceinline__ float lin_start(const v16f& a, int r) { return a[kPieces * (r / 2) + (r & 1)]; }
+
+// Pieces 2.. of pair p's row on this lane half added to the combined head sum x, in order.
+__device__ __forceinline__ float add_lin_rest(const v16f& a, int p, float x) {
 #pragma unroll
-  for (int c = 1; c < kPieces; ++c) x = x + a[s + c];
+  for (int c = 2; c < kPieces; ++c) x = x + a[kPieces * p + c];
   return x;
 }
 
@@ -707,7 +711,10 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
   auto reduce = [&](const Acc& a, float kscale_f, float* sc) {
     float part[RW];
 #pragma unroll
-    for (int r = 0; r < RW; ++r) part[r] = 0.0f;
+    for (int r = 0; r < RW; ++r) {
+      if constexpr (kSplit) part[r] = lin_start(a.lin, r);
+      else part[r] = 0.0f;
+    }
 #pragma unroll
     for (int mt = 0; mt < H / 32; ++mt)
 #pragma unroll
@@ -719,7 +726,7 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
     for (int p = 0; p < NP; ++p) {
       const float hs = combine_halves(part[2 * p], part[2 * p + 1]);
       // KS = false: no key scales (every factor 1.0, so the product is skipped, not changed)
-      if constexpr (kSplit) sc[p] = KS ? (lin_of_pair(a.lin, p) + hs) * kscale_f : lin_of_pair(a.lin, p) + hs;
+      if constexpr (kSplit) sc[p] = KS ? add_lin_rest(a.lin, p, hs) * kscale_f : add_lin_rest(a.lin, p, hs);
       else sc[p] = KS ? hs * kscale_f : hs;
     }
   };
