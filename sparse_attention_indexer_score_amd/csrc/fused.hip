@@ -387,44 +387,41 @@ __device__ __forceinline__ float relu_bits(float x) { return clamp0(x); }
 // Key tiles are staged through LDS: all four waves of a workgroup use the same keys, so a
 // stage of 32-key tiles is fetched once per workgroup with 16-byte loads straight into LDS
 // (issued one stage ahead, double-buffered, one barrier per stage) and each wave reads its
-// MFMA key operands from LDS.  A 16-byte LDS read phase takes 8 (or 16) lanes, i.e. 8 (16)
-// consecutive keys at the same 16-byte part, which the layout puts in distinct banks.
-// fp4: one region per K-step, [ks][key][32 bytes], the two 16-byte halves of key k's row
-// swapped when g(k) = 1, so that a stage is a dense copy of its keys in another order: a
-// lane's load offset is the same in every stage, and K-step 1 sits a constant distance
-// from K-step 0.  e4m3: rows padded to 144 bytes (a row stride of 9 parts).  A stage is 8
-// fp4 tiles (16 KB) or 4 e4m3 tiles (18 KB), which keeps two workgroups per CU within LDS.
+// MFMA key operands from LDS.  A stage is kept in regions of 32-byte rows, one region per
+// 16-byte part that a lane half reads of a key for one MFMA operand: fp4 has one region per
+// K-step, e4m3 two (the two 16-byte loads of a K-step).  Row k of a region holds that part
+// for lane halves 0 and 1, swapped when g(k) = 1: a 16-byte read phase takes 8 (or 16)
+// lanes, i.e. 8 (16) consecutive keys at one half, which this puts in distinct banks over
+// 128 (256) bytes.  A stage is then a dense copy of its keys in another order, so a lane's
+// load offset is the same in every stage, and every operand read of a lane sits a constant
+// distance from its first.  A stage is 8 fp4 tiles or 4 e4m3 tiles (16 KB either way),
+// which keeps two workgroups per CU within LDS.
 template <int FMT>
 struct StageGeom {
-  static constexpr bool kSwz = FMT == FMT_MXFP4;            // K-step regions (else padded rows)
   static constexpr int kTiles = FMT == FMT_MXFP4 ? 8 : 4;  // tiles per stage
   static constexpr int kKB = Fmt<FMT>::kBytes;
-  static constexpr int kParts = kKB / 16;                   // 16-byte parts of a key
   static constexpr int kKeys = kTiles * kTile;             // keys per stage
-  static constexpr int kRow = kSwz ? kKB / 2 : kKB + 16;    // bytes per LDS row
-  static constexpr int kSlotsPerRow = kRow / 16;
-  static constexpr int kBytes = kKeys * (kSwz ? kKB : kRow);  // codes of one stage
-  static constexpr int kStepOff = kSwz ? kKeys * kRow : 64;   // K-step 1 from K-step 0
+  static constexpr int kRow = 32;                          // bytes per region row
+  static constexpr int kRegion = kKeys * kRow;             // bytes per region
+  static constexpr int kBytes = kKeys * kKB;               // codes of one stage
+  static constexpr int kStepOff = FMT == FMT_MXFP4 ? kRegion : 2 * kRegion;  // K-step 1 from 0
+  static constexpr int kHalfBytes = FMT == FMT_MXFP4 ? 16 : 32;  // a lane half's bytes per K-step
   // Half swap of stage key k (k mod 16 decides: stage and tile starts are multiples of 16
   // keys).  Keys k and k + 4 of an 8-key phase share banks otherwise (32-byte rows over 128
   // bytes of banks), as do keys k and k + 8 of a 16-key phase over 256 bytes.
   static __device__ __forceinline__ int g(int k) { return ((k >> 2) ^ (k >> 3)) & 1; }
-  // Byte offset of lane (col, half)'s K-step 0 part within a tile.
-  static __device__ __forceinline__ int lane_off(int col, int half) {
-    if constexpr (kSwz) return col * kRow + ((half ^ g(col)) * 16);
-    else return col * kRow + half * 32;
+  // Byte offset of lane (col, half)'s first operand part within a tile.
+  static __device__ __forceinline__ int lane_off(int col, int half) { return col * kRow + ((half ^ g(col)) * 16); }
+  // Byte offset within a key's codes of the part that region R holds for lane half h.
+  static __device__ __forceinline__ int part_off(int R, int h) {
+    if constexpr (FMT == FMT_MXFP4) return R * 32 + h * 16;                       // K-step R
+    else return (R >> 1) * 64 + h * 32 + (R & 1) * 16;                          // K-step R / 2
   }
-  // Key and part that LDS slot sidx of a stage holds (pad slots: part 0 of their key again).
-  static __device__ __forceinline__ int slot_key(int sidx) {
-    if constexpr (kSwz) return (sidx % (2 * kKeys)) / 2;
-    else return sidx / kSlotsPerRow;
-  }
-  static __device__ __forceinline__ int slot_part(int sidx) {
-    if constexpr (kSwz) return 2 * (sidx / (2 * kKeys)) + ((sidx & 1) ^ g(slot_key(sidx)));
-    else {
-      const int part = sidx % kSlotsPerRow;
-      return part < kParts ? part : 0;
-    }
+  // Key and byte offset within it that 16-byte LDS slot sidx (>= 0) of a stage holds.
+  static_assert((kKeys & (kKeys - 1)) == 0, "power-of-two stage");
+  static __device__ __forceinline__ int slot_key(int sidx) { return (int)(((uint32_t)sidx % (2 * kKeys)) >> 1); }
+  static __device__ __forceinline__ int slot_off(int sidx) {
+    return part_off((int)((uint32_t)sidx / (2 * kKeys)), (sidx & 1) ^ g(slot_key(sidx)));
   }
 };
 
@@ -674,7 +671,7 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
     for (int ks = 0; ks < 2; ++ks) {
       if constexpr (FMT == FMT_E4M3) {
         const v4i x0 = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(row + ks * G::kStepOff);
-        const v4i x1 = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(row + ks * G::kStepOff + 16);
+        const v4i x1 = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(row + ks * G::kStepOff + G::kRegion);
         ko.b[ks] = v8i{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
       } else {
         const v4i x = *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(row + ks * G::kStepOff);
@@ -744,7 +741,7 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
 
   // Stage loads straight into LDS (global_load_lds_dwordx4): lane l of wave w writes the 16
   // bytes it fetches to the wave's LDS base + 16 l, so each lane is given the global piece
-  // that belongs in its 16-byte slot of the stage layout (G::slot_key, G::slot_part).
+  // that belongs in its 16-byte slot of the stage layout (G::slot_key, G::slot_off).
   // Block scales and key scales come by 4-byte loads.
   constexpr int kSlots = G::kBytes / 16;
   constexpr int kSlotIters = (kSlots + kThreads - 1) / kThreads;
@@ -776,7 +773,7 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
             const int sidx = s0 + ln;
             const int key = min(phase + (kpos0 + G::slot_key(sidx)) * S, lmax);
             const int32_t id = sl.pages[(key >> 6) - pbase];
-            const int32_t off = (key & (kPage - 1)) * KB + G::slot_part(sidx) * 16;
+            const int32_t off = (key & (kPage - 1)) * KB + G::slot_off(sidx);
             __builtin_amdgcn_global_load_lds(
                 (const __attribute__((address_space(1))) void*)(A.k + (int64_t)id * (kPage * KB) + off),
                 lds_dst(lbase + s0 * 16), 16, 0, 0);
@@ -795,32 +792,38 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
         return;
       }
     }
-    if constexpr (G::kSwz && MODE != MODE_SAMPLE) {  // sample positions are strided
-      // Contiguous keys with the whole stage inside the key array: the stage holds the 64-byte
-      // rows of kKeys consecutive keys, so a lane's source is the stage's first key plus an
-      // offset of its own.  Load u fills K-step u / 2 of keys [128 (u % 2), +128); a wave's
-      // 64 slots there are 32 whole keys, 16-key aligned, so the half swap depends on the
-      // lane alone.  The lane offset is formed anew in each stage (no register held across
-      // the tile loop) and added to a wave-uniform base.
+    if constexpr (MODE != MODE_SAMPLE && !SHARED) {  // not strided sample positions, not paged keys
+      // Contiguous keys with the whole stage inside the key array: the stage holds the codes
+      // of kKeys consecutive keys, so a lane's source is the stage's first key plus an offset
+      // of its own.  Load u fills region u * kThreads / (2 kKeys) for a run of 128 keys; a
+      // wave's 64 slots there are 32 whole keys, 16-key aligned, so the half swap depends on
+      // the lane alone.  The lane offset is formed anew in each stage (no register held
+      // across the tile loop) and added to a wave-uniform base.
       const int64_t kfirst = (int64_t)phase + pos0;
       if (req < 0 && S == 1 && kfirst + G::kKeys - 1 <= last_key) {  // wave-uniform
-        static_assert(kSlots == 4 * kThreads && G::kKeys == 2 * 128, "four loads of 128 keys' K-step halves");
+        static_assert(kSlots == 4 * kThreads && 2 * G::kKeys % kThreads == 0, "whole regions per load");
         int lv = l;
         asm volatile("" : "+v"(lv));
         const int kq = lv >> 1;
-        const uint32_t loff = (uint32_t)(kq * KB + (((lv & 1) ^ G::g(kq)) * 16));
+        const uint32_t loff = (uint32_t)(kq * KB + ((lv & 1) ^ G::g(kq)) * G::kHalfBytes);
         const uint8_t* gb = A.k + kfirst * KB + wave * (kWave / 2) * KB;
 #pragma unroll
-        for (int u = 0; u < kSlotIters; ++u)
-          __builtin_amdgcn_global_load_lds(
-              (const __attribute__((address_space(1))) void*)(gb + (loff + (uint32_t)((u & 1) * 128 * KB + (u >> 1) * (KB / 2)))),
-              lds_dst(lbase + (u * kThreads + wave * kWave) * 16), 16, 0, 0);
-        const int64_t gk = kfirst + wave * kWave;
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(A.k_sf + gk * 4 + (uint32_t)(lv * 4)),
-                                         lds_dst(sl.sf + buf * G::kKeys + wave * kWave), 4, 0, 0);
-        if (has_ks)
-          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(A.k_scale + gk + (uint32_t)lv),
-                                           lds_dst(sl.ks + buf * G::kKeys + wave * kWave), 4, 0, 0);
+        for (int u = 0; u < kSlotIters; ++u) {
+          constexpr int kRegionSlots = 2 * G::kKeys;
+          const int R = u * kThreads / kRegionSlots, kb = (u * kThreads % kRegionSlots) / 2;
+          const uint32_t ucst = (uint32_t)(kb * KB + G::part_off(R, 0));
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(gb + (loff + ucst)),
+                                           lds_dst(lbase + (u * kThreads + wave * kWave) * 16), 16, 0, 0);
+        }
+        if (G::kKeys >= kThreads || wave * kWave < G::kKeys) {  // wave-uniform (every wave's for fp4)
+          const int64_t gk = kfirst + wave * kWave;
+          if constexpr (FMT == FMT_MXFP4)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(A.k_sf + gk * 4 + (uint32_t)(lv * 4)),
+                                             lds_dst(sl.sf + buf * G::kKeys + wave * kWave), 4, 0, 0);
+          if (has_ks)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(A.k_scale + gk + (uint32_t)lv),
+                                             lds_dst(sl.ks + buf * G::kKeys + wave * kWave), 4, 0, 0);
+        }
         return;
       }
     }
@@ -829,7 +832,7 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
       const int s0 = u * kThreads + wave * kWave;
       if (s0 < kSlots) {  // wave-uniform
         const int sidx = s0 + ln;
-        const uint8_t* src = A.k + key_of(pos0 + G::slot_key(sidx)) * KB + G::slot_part(sidx) * 16;
+        const uint8_t* src = A.k + key_of(pos0 + G::slot_key(sidx)) * KB + G::slot_off(sidx);
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                          lds_dst(lbase + s0 * 16), 16, 0, 0);
       }
@@ -875,6 +878,10 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
         // (into the registers they have just read), so the LDS latency runs under this
         // tile's head reduce instead of stalling the next tile's MFMAs.
         const int i0 = SHARED ? slot : 0;
+        // Pins the loop's code to an 8-byte boundary: the MXFP4 filter loop ran 1.3 % slower
+        // with its code 4 bytes off this placement (every offset measured), the e4m3 loops
+        // showed no difference.  Costs at most one s_nop per stage.
+        asm volatile(".p2align 3");
         KeyOperand ko;
         float ksc;
         read_b(sbase, i0, ko, ksc);
