@@ -49,11 +49,8 @@ int sample_stride_for(int k) {
   return s < 1 ? 1 : s;
 }
 
-// Sample phase: one per call, hashed so that it does not line up with periodic data, and
-// the same for every row, so that the row blocks of a key chunk gather the same sample keys
-// (from L2 after the first).  Each row's samples are a strided subset of its keys either way.
-__device__ __forceinline__ int sample_phase(int stride) {
-  uint32_t x = (uint32_t)stride * 0x9E3779B9u + 0x7F4A7C15u;
+__device__ __forceinline__ int sample_phase(int row_block, int stride) {
+  uint32_t x = (uint32_t)row_block * 0x9E3779B9u + 0x7F4A7C15u;
   x ^= x >> 16;
   x *= 0x85EBCA6Bu;
   x ^= x >> 13;
@@ -960,7 +957,7 @@ __global__ __launch_bounds__(kThreads, 2) void score_tiles_kernel(ScoreArgs A, L
   const int chunk = (int)(item / W.nrb);
   const int wave = uniform(threadIdx.x / kWave);
   const int S = (MODE == MODE_SAMPLE) ? E.stride : 1;
-  const int phase = (MODE == MODE_SAMPLE) ? sample_phase(S) : 0;
+  const int phase = (MODE == MODE_SAMPLE) ? sample_phase(rb, S) : 0;
   const int c0 = chunk * W.chunk, c1 = c0 + W.chunk;
   // Tiles of the workgroup: the union of all its rows' ranges within the chunk.
   int lo = 0x7FFFFFFF, hi = 0;
@@ -1017,7 +1014,7 @@ __global__ __launch_bounds__(kThreads, 2) void score_pages_kernel(ScoreArgs A, L
       const int chunk = (int)(item / W.nrb);
       const int base = 4 * rb;
       const int S = (MODE == MODE_SAMPLE) ? E.stride : 1;
-      const int phase = (MODE == MODE_SAMPLE) ? sample_phase(S) : 0;
+      const int phase = (MODE == MODE_SAMPLE) ? sample_phase(rb, S) : 0;
       const int c0 = chunk * W.chunk, c1 = c0 + W.chunk;
       const int wave = uniform(threadIdx.x / kWave);
       const StageLds<FMT> sl{sh.codes, sh.sf, sh.ks, cand.s, cand.i, pages};
@@ -1088,7 +1085,7 @@ struct ThrArgs {
   int32_t* cnt;
   long long* stats;
   int32_t* fb_ctrl;
-  int32_t rows, k, cap, ns, stride;
+  int32_t rows, k, cap, ns, stride, rb_rows;
   int32_t debug_mode, debug_row_mod;
 };
 
@@ -1116,7 +1113,7 @@ __global__ __launch_bounds__(kThrThreads) void threshold_kernel(ThrArgs T) {
   } else if (V <= T.cap) {
     tr = -__builtin_inff();
   } else {
-    const int p = sample_phase(T.stride);
+    const int p = sample_phase(r / T.rb_rows, T.stride);
     int jlo, jhi;
     sample_range(ks, ke, p, T.stride, jlo, jhi);
     const int n = jhi - jlo;
@@ -1618,6 +1615,7 @@ hipError_t launch_fused(const DevProblem& P, const FusedPlan& F, int32_t* out_id
     T.cap = F.cap;
     T.ns = F.ns;
     T.stride = F.stride;
+    T.rb_rows = rows_per_block_for(P);
     T.debug_mode = F.debug_mode;
     T.debug_row_mod = F.debug_row_mod;
     if (F.ns >= 2048)
