@@ -766,18 +766,27 @@ __device__ __forceinline__ void wg_tiles(const ScoreArgs& A, const LinArgs& L, c
       // stages reach, times the stride, stays below 2^31.
       if (req >= 0 && pg_cached && fits32) {  // wave-uniform
         const int kpos0 = (int)pos0, pbase = (int)pg_lo;
+        // Load u fills region u kThreads / (2 kKeys) for the run of 128 stage keys starting at
+        // (u kThreads mod 2 kKeys) / 2, and this lane's slot there holds stage key
+        // run + kq, half h: the page lookup is made once per run (one for e4m3, two for fp4)
+        // and the loads differ only in the part.
+        static_assert(kSlots == 4 * kThreads && 2 * G::kKeys % kThreads == 0, "whole regions per load");
+        constexpr int kRuns = 2 * G::kKeys / kThreads;
+        const int kq = wave * (kWave / 2) + (ln >> 1);
+        const int h = (ln & 1) ^ G::g(kq);
+        const uint8_t* src[kRuns];
+#pragma unroll
+        for (int j = 0; j < kRuns; ++j) {
+          const int key = min(phase + (kpos0 + j * (kThreads / 2) + kq) * S, lmax);
+          const int32_t id = sl.pages[(key >> 6) - pbase];
+          src[j] = A.k + (int64_t)id * (kPage * KB) + (key & (kPage - 1)) * KB;
+        }
 #pragma unroll
         for (int u = 0; u < kSlotIters; ++u) {
-          const int s0 = u * kThreads + wave * kWave;
-          if (s0 < kSlots) {
-            const int sidx = s0 + ln;
-            const int key = min(phase + (kpos0 + G::slot_key(sidx)) * S, lmax);
-            const int32_t id = sl.pages[(key >> 6) - pbase];
-            const int32_t off = (key & (kPage - 1)) * KB + G::slot_off(sidx);
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void*)(A.k + (int64_t)id * (kPage * KB) + off),
-                lds_dst(lbase + s0 * 16), 16, 0, 0);
-          }
+          constexpr int kRegionSlots = 2 * G::kKeys;
+          const int R = u * kThreads / kRegionSlots, j = (u * kThreads % kRegionSlots) / kThreads;
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src[j] + G::part_off(R, h)),
+                                           lds_dst(lbase + (u * kThreads + wave * kWave) * 16), 16, 0, 0);
         }
         if (wave * kWave < G::kKeys) {
           const int key = min(phase + (kpos0 + wave * kWave + ln) * S, lmax);
