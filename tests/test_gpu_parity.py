@@ -228,6 +228,27 @@ def test_edge_lengths_e4m3():
     assert_same_sets(sai.idx_fused_topk(dp, 512).cpu().numpy(), ref, "fused")
 
 
+@pytest.mark.parametrize("fmt,num_keys", [("e4m3", 127), ("e4m3", 128), ("e4m3", 129), ("e4m3", 1000),
+                                          ("mxfp4", 255), ("mxfp4", 256), ("mxfp4", 257), ("mxfp4", 1800)])
+def test_stage_boundaries_at_key_array_end(fmt, num_keys):
+    """Key tiles are staged 128 (e4m3) or 256 (MXFP4) keys at a time from a workgroup's first
+    tile: a stage wholly inside the key array is loaded as a dense copy, one that reaches past
+    its end through the per-key clamped path.  Key counts just below, at and above a stage,
+    rows starting at different tiles and some ending early put the array's end at every
+    kind of position in the last stage; scores of every row against the oracle, selection
+    bit-exact over the GPU's scores (k = 64: rows over 256 keys are sampled)."""
+    rows = 24
+    if fmt == "e4m3":
+        p = wl.prefill(rows=rows, num_keys=num_keys, topk=64, seed=500 + num_keys)
+    else:
+        p = wl.long_context(rows=rows, num_keys=num_keys, band_keys=64, topk=64, seed=500 + num_keys)
+    r = np.arange(rows)
+    p.ke = (num_keys - (r % 3) * (r % 5)).astype(np.int32)
+    p.ks = np.minimum((r * 37) % max(1, num_keys // 2), p.ke).astype(np.int32)
+    st = full_check(p, 64, score_rows=range(rows))
+    assert st["rows_sampled"] + st["rows_store_all"] == rows
+
+
 def test_select_all_equal_rows_force_rescan():
     rows, ld = 3, 131072
     x = np.full((rows, ld), 0.5, dtype=np.float32)
